@@ -1,0 +1,10 @@
+"""Float64 CPU oracle for FLCE (test infrastructure only; never on the product path)."""
+from .flce_oracle import (  # noqa: F401
+    ce_ref,
+    check_targets,
+    flce_brute_force,
+    flce_ref,
+    flce_rows_ref,
+    row_lse,
+    valid_rows,
+)
