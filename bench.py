@@ -1,0 +1,208 @@
+"""Benchmark: fused linear + cross-entropy forward+backward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config llama3] [--no-cpu-baseline]
+
+One step = one flce_fwd_bwd call over the whole batch of the workload (all
+token chunks: logits GEMM with the softmax-statistics epilogue, log-sum-exp,
+in-place gradient, dX and dW GEMMs, final mean).  Inputs are seeded synthetic
+tensors already resident in HBM when the timed region starts.  Prints one JSON
+line on stdout (progress goes to stderr).
+
+The default workload is the Llama-3-8B-shaped head: BT=8192 tokens (batch 8 x
+sequence 1024), H=4096, V=128256, bf16 inputs, fp32 accumulation, Zipf(1.1)
+targets with 5% ignored, one 4096-token chunk (<= 1 GiB) at a time.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published (no sparsity)
+PEAK_HBM_GBS = 8000.0
+METRIC = "FLCE fwd+bwd tokens/s and % bf16 MFMA peak at H=4096, V=128256"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def gpu_bench(w, steps, warmup):
+    import torch
+
+    import linear_cross_entropy_05_amd as flce
+    import synth_inputs as si
+
+    dev = torch.device("cuda", 0)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"[bench] device {props.name} {getattr(props, 'gcnArchName', '?')} CUs={props.multi_processor_count}")
+    log(f"[bench] inputs {w.name}: BT={w.BT} H={w.H} V={w.V} {w.dtype}")
+    X, W, y = si.make_inputs(w)
+    Xd, Wd, yd = X.to(dev), W.to(dev), y.to(dev)
+    del X, W
+    C = flce.flce_chunk_tokens(w.BT, w.H, w.V, w.chunk_tokens, w.torch_dtype)
+    ws_bytes = flce.flce_workspace_bytes(w.BT, w.H, w.V, w.chunk_tokens, w.torch_dtype)
+    out = (
+        torch.empty((), dtype=torch.float32, device=dev),
+        torch.empty_like(Xd),
+        torch.empty((w.V, w.H), dtype=torch.float32, device=dev),
+        torch.empty((1,), dtype=torch.int32, device=dev),
+    )
+    torch.cuda.synchronize()
+
+    # peak extra memory of one call: everything it allocates beyond inputs/outputs
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    flce.flce_fwd_bwd(Xd, Wd, yd, w.ignore_index, w.chunk_tokens, out=out, check=True)
+    torch.cuda.synchronize()
+    peak_extra = torch.cuda.max_memory_allocated(dev) - base
+    log(f"[bench] chunk={C} workspace={ws_bytes / 2**30:.3f} GiB peak_extra={peak_extra / 2**30:.3f} GiB "
+        f"loss={out[0].item():.6f}")
+
+    workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        flce.flce_fwd_bwd(Xd, Wd, yd, w.ignore_index, w.chunk_tokens, out=out, workspace=workspace, check=False)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {warmup} done; timing {steps} steps")
+
+    stream = torch.cuda.current_stream(dev)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    with flce.KernelTimer(max_launches=64 * steps + 64) as kt:
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t0.record(stream)
+        for _ in range(steps):
+            flce.flce_fwd_bwd(Xd, Wd, yd, w.ignore_index, w.chunk_tokens, out=out, workspace=workspace, check=False)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        wall1 = time.perf_counter()
+    ms = t0.elapsed_time(t1) / steps
+    wall_ms = (wall1 - wall0) * 1e3 / steps
+    err = int(out[3].item())
+    if err != 0:
+        raise RuntimeError(f"device reported error flag {err}")
+    loss = float(out[0].item())
+    kernels = {k: {"avg_ms": kt.ms[k] / kt.launches[k], "launches_per_step": kt.launches[k] / steps,
+                   "ms_per_step": kt.ms[k] / steps}
+               for k in kt.ms if kt.launches[k]}
+    log(f"[bench] {ms:.3f} ms/step (wall {wall_ms:.3f}); kernels: "
+        + ", ".join(f"{k} {v['ms_per_step']:.3f}" for k, v in kernels.items()))
+    return {"ms": ms, "C": C, "ws_bytes": ws_bytes, "peak_extra": peak_extra, "loss": loss, "kernels": kernels,
+            "cus": props.multi_processor_count, "arch": getattr(props, "gcnArchName", "?")}
+
+
+def roofline(w, r):
+    """Dominant kernel (largest time per step) against its own roofline."""
+    name, k = max(r["kernels"].items(), key=lambda kv: kv[1]["ms_per_step"])
+    C = r["C"]
+    nchunks = -(-w.BT // C)
+    per_launch_flops = {
+        # each GEMM launch covers one chunk: 2 * tokens * H * V
+        "logits": 2.0 * w.BT * w.H * w.V / nchunks,
+        "dx": 2.0 * w.BT * w.H * w.V / nchunks,
+        "dw": 2.0 * w.BT * w.H * w.V / nchunks,
+    }
+    esz = 2 if w.dtype == "bf16" else 4
+    per_launch_bytes = {
+        # one chunk of logits read + gradient written, in place
+        "grad_inplace": 2.0 * (w.BT / nchunks) * w.V * esz,
+    }
+    if name in per_launch_flops:
+        achieved = per_launch_flops[name] / (k["avg_ms"] * 1e-3) / 1e12
+        return name, {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    achieved = per_launch_bytes.get(name, 0.0) / (k["avg_ms"] * 1e-3) / 1e9
+    return name, {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                  "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+
+
+def cpu_baseline(w, sample_tokens):
+    """The float64 oracle on the host cores, on the first `sample_tokens` tokens
+    of the same workload (full W), as tokens/s."""
+    import numpy as np
+
+    import oracle
+    import synth_inputs as si
+
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    cores = len(os.sched_getaffinity(0))
+    X, W, y = si.make_inputs(w)
+    S = min(sample_tokens, w.BT)
+    Xs, ys = X[:S].clone(), y[:S].clone()
+    log(f"[bench] cpu oracle on {S} tokens, {cores} cores")
+    with threadpool_limits(limits=cores):
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = int(blas[0].get("num_threads", cores)) if blas else cores
+        t0 = time.perf_counter()
+        ref = oracle.flce_ref(Xs, W, ys, w.ignore_index)
+        dt = time.perf_counter() - t0
+    log(f"[bench] cpu oracle {dt:.2f} s (loss on sample {ref['loss']:.5f})")
+    return {"value": round(S / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {S} of {w.BT} tokens of the {w.name} workload with the full W "
+                      f"[{w.V}, {w.H}]; NumPy float64 fwd+bwd, {dt:.2f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="llama3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        return 2
+
+    import synth_inputs as si
+
+    w = si.workload(a.config)
+    r = gpu_bench(w, a.steps, a.warmup)
+    tokens_per_s = w.BT / (r["ms"] * 1e-3)
+    tflops = 6.0 * w.BT * w.H * w.V / (r["ms"] * 1e-3) / 1e12
+    dom, roof = roofline(w, r)
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(r["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}-head", "tokens": w.BT, "hidden": w.H, "vocab": w.V,
+                   "chunk_tokens": r["C"], "ignore_frac": w.ignore[1] if len(w.ignore) > 1 else 0,
+                   "targets": w.targets},
+        "tflops": round(tflops, 2),
+        "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "peak_extra_bytes": int(r["peak_extra"]),
+        "workspace_bytes": int(r["ws_bytes"]),
+        "dominant_kernel": dom,
+        "roofline": roof,
+        "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in r["kernels"].items()},
+        "device": {"arch": r["arch"], "cus": r["cus"]},
+        "loss": r["loss"],
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, a.cpu_sample_tokens)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,132 @@
+/*
+ * flce.h -- C ABI of the MI355X (gfx950) fused linear + cross-entropy library.
+ *
+ * What is computed.  For hidden states X [BT, H], an output-projection weight
+ * W [V, H] (the nn.Linear(H, V).weight layout, no bias) and integer targets
+ * y [BT]:
+ *
+ *     Z = X W^T,  lse_i = ln sum_v exp(Z_iv),  l_i = lse_i - Z_{i, y_i},
+ *     N = #{i : y_i != ignore_index},  loss = sum_{valid i} l_i / N,
+ *     G_iv = (exp(Z_iv - lse_i) - [v == y_i]) / N   (0 on ignored rows),
+ *     dX = G W,  dW = G^T X.
+ *
+ * This is the fused Linear+CrossEntropy (FLCE) loss of "[論文レビュー] Liger
+ * Kernel: Efficient Triton Kernels for LLM Training" (nubint.ai), section
+ * 提案手法: the tokens are taken in chunks so that the BT x V logits are never
+ * held whole; within a chunk the softmax statistics come from an online
+ * max / sum-of-exponentials and the logits are overwritten by their gradient
+ * (section 主な発見).  "Liger-Kernel 項目詳細介紹" (aibars.net), section
+ * 技術實現, states that the computation is exact; section 使用方法, item 3,
+ * fixes the call shape: loss_fn(weight, input, target), weight first.  The
+ * softmax cross-entropy formulas themselves are the textbook definition.
+ *
+ * Readings of what the pages leave open: the reduction is the mean over the
+ * non-ignored tokens of the whole call; N = 0 gives loss 0 and zero
+ * gradients; a non-ignored target outside [0, V) is an error.
+ *
+ * Conventions for every entry point.
+ *   - All array pointers are DEVICE pointers owned by the caller; the library
+ *     allocates nothing and keeps no state between calls (apart from a
+ *     per-device "is this a gfx950" answer).  Row-major, densely packed.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  Results are valid once the stream has been synchronised.
+ *   - Problems detectable on the host are reported by the return value
+ *     before anything is launched or written.  A non-ignored target outside
+ *     [0, V) is detected on the device: *err_flag is set to FLCE_ERR_TARGET
+ *     (and to 0 otherwise) and the numeric outputs are then unspecified.
+ *   - Two calls may run concurrently only with distinct workspaces and
+ *     outputs.  Inputs are never written (except `logits` in the in-place call).
+ */
+#ifndef FLCE_H
+#define FLCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of X, W (and dX).  Accumulation is always fp32. */
+enum flce_dtype { FLCE_F32 = 0, FLCE_BF16 = 1 };
+
+/* Status codes. */
+enum flce_status {
+  FLCE_OK = 0,
+  FLCE_ERR_ARG = 1,       /* null pointer, negative or zero size */
+  FLCE_ERR_DTYPE = 2,     /* dtype not one of flce_dtype */
+  FLCE_ERR_WORKSPACE = 3, /* workspace_bytes below what *_workspace_bytes returns */
+  FLCE_ERR_DEVICE = 4,    /* current device is not gfx950 */
+  FLCE_ERR_LAUNCH = 5,    /* a kernel launch failed */
+  FLCE_ERR_TARGET = 6,    /* (device-side, via *err_flag) target out of range */
+  FLCE_ERR_SHAPE = 7,     /* H not a multiple of 8 (bf16) or 4 (fp32) */
+  FLCE_ERR_ALIGN = 8      /* X, W or workspace not 16/16/256-byte aligned, targets not 8 */
+};
+
+/* Tokens per chunk that flce_fwd_bwd will use: chunk_tokens if positive
+ * (capped at BT), else the largest power of two whose logits chunk
+ * (chunk x round_up(V, 256) elements of the dtype) fits in 1 GiB, capped at BT.
+ * Returns 0 for invalid arguments. */
+int64_t flce_chunk_tokens(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);
+
+/* Bytes of device workspace flce_fwd_bwd needs for these sizes: one logits
+ * chunk (chunk x round_up(V, 256) elements of the dtype) plus per-token and
+ * per-tile statistics (O(chunk x V / 256) floats) and, when the dX product
+ * is split along the vocabulary, fp32 partials bounded by half the chunk.
+ * This is the whole extra memory of the call.  Returns 0 for invalid args. */
+size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);
+
+/* Fused linear + cross-entropy, forward and backward, in one call.
+ *   X        [BT, H] dtype, 16-byte aligned        (may be NULL if BT == 0)
+ *   W        [V, H]  dtype, 16-byte aligned
+ *   targets  [BT]    int64, values in [0, V) or ignore_index
+ *   loss     device float scalar: sum of token losses / N (0 when N == 0)
+ *   row_loss [BT] float or NULL: per-token loss l_i (0 on ignored tokens)
+ *   dX       [BT, H] dtype: d loss / d X          (may be NULL if BT == 0)
+ *   dW       [V, H]  float: d loss / d W, fp32 (overwritten, not accumulated into)
+ *   workspace, workspace_bytes: >= flce_workspace_bytes(...), 256-byte aligned
+ *   err_flag device int32: 0, or FLCE_ERR_TARGET after the call completes
+ * Gradients are for an upstream gradient of 1; scale them for another. */
+int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H, int64_t V,
+                 int64_t ignore_index, int64_t chunk_tokens, int dtype, float* loss, float* row_loss, void* dX,
+                 float* dW, void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream);
+
+/* Bytes of device workspace ce_fwd_bwd_inplace needs (a counter, and BT
+ * floats of per-token loss when row_loss is NULL). */
+size_t ce_workspace_bytes(int64_t BT, int64_t V);
+
+/* Logits-only cross-entropy, forward and backward, in place: the CrossEntropy
+ * kernel of the same review page (主な発見): online softmax per row, then the
+ * fp32 logits [BT, V] are overwritten by d loss / d logits
+ * = (softmax - onehot) / N (rows with ignored targets become 0).
+ *   logits   [BT, V] float, 4-byte aligned (any V)
+ *   targets, ignore_index, loss, row_loss, err_flag, stream: as above. */
+int ce_fwd_bwd_inplace(float* logits, const int64_t* targets, int64_t BT, int64_t V, int64_t ignore_index,
+                       float* loss, float* row_loss, void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                       void* stream);
+
+/* Per-kernel timing, for benchmarks and profilers (process-global, not
+ * thread-safe, off by default).  flce_profile_begin(max_launches) creates
+ * 2 x max_launches HIP events and turns timing on: from then on every kernel
+ * the library launches is bracketed by two event records on its own stream
+ * (launches beyond max_launches are not timed).  flce_profile_end waits for
+ * the recorded events, turns timing off, frees the events and writes, for
+ * each kernel kind p < n, the summed duration in ms and the number of timed
+ * launches.  Kinds: 0 target count, 1 logits GEMM + softmax statistics,
+ * 2 log-sum-exp, 3 in-place logits gradient, 4 dX GEMM, 5 dX split sum,
+ * 6 dW GEMM, 7 final mean, 8 logits-only cross-entropy rows, 9 zero fill. */
+#define FLCE_NUM_KERNEL_KINDS 10
+int flce_profile_begin(int max_launches);
+int flce_profile_end(double* total_ms, int64_t* launches, int n);
+
+/* Static English text for a status code. */
+const char* flce_status_str(int status);
+
+/* 1 if device `device` (a HIP ordinal) is a gfx950, 0 if not, -1 on error. */
+int flce_device_supported(int device);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H */

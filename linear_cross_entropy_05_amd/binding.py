@@ -1,0 +1,266 @@
+"""Python binding of libflce (ctypes): argument marshalling only.
+
+Every step of the loss runs in the HIP kernels behind ``include/flce.h``;
+this module checks tensors, allocates outputs and the workspace through
+PyTorch's caching allocator, and passes raw device pointers and the current
+HIP stream.  There is no CPU or PyTorch fallback: if the library is missing
+or the device is not a gfx950, the call raises.
+
+The module form follows the low-level usage shown on "Liger-Kernel 項目詳細介紹"
+(使用方法, item 3): ``loss_fn(weight, input, target)`` with the weight first,
+then ``loss.backward()``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libflce.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "flce.h")
+
+FLCE_F32, FLCE_BF16 = 0, 1
+STATUS = {
+    0: "FLCE_OK",
+    1: "FLCE_ERR_ARG",
+    2: "FLCE_ERR_DTYPE",
+    3: "FLCE_ERR_WORKSPACE",
+    4: "FLCE_ERR_DEVICE",
+    5: "FLCE_ERR_LAUNCH",
+    6: "FLCE_ERR_TARGET",
+    7: "FLCE_ERR_SHAPE",
+    8: "FLCE_ERR_ALIGN",
+}
+_DTYPES = {torch.float32: FLCE_F32, torch.bfloat16: FLCE_BF16}
+
+_lib = None
+
+
+class FlceError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = _lib.flce_status_str(status).decode() if _lib is not None else STATUS.get(status, "?")
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({msg})" if what else msg)
+
+
+def _declare(lib):
+    c = ctypes
+    i64, vp, sz = c.c_int64, c.c_void_p, c.c_size_t
+    lib.flce_chunk_tokens.argtypes = [i64, i64, i64, i64, c.c_int]
+    lib.flce_chunk_tokens.restype = i64
+    lib.flce_workspace_bytes.argtypes = [i64, i64, i64, i64, c.c_int]
+    lib.flce_workspace_bytes.restype = sz
+    lib.flce_fwd_bwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, c.c_int, vp, vp, vp, vp, vp, sz, vp, vp]
+    lib.flce_fwd_bwd.restype = c.c_int
+    lib.ce_workspace_bytes.argtypes = [i64, i64]
+    lib.ce_workspace_bytes.restype = sz
+    lib.ce_fwd_bwd_inplace.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, sz, vp, vp]
+    lib.ce_fwd_bwd_inplace.restype = c.c_int
+    lib.flce_status_str.argtypes = [c.c_int]
+    lib.flce_status_str.restype = c.c_char_p
+    lib.flce_device_supported.argtypes = [c.c_int]
+    lib.flce_device_supported.restype = c.c_int
+    lib.flce_profile_begin.argtypes = [c.c_int]
+    lib.flce_profile_begin.restype = c.c_int
+    lib.flce_profile_end.argtypes = [c.POINTER(c.c_double), c.POINTER(c.c_int64), c.c_int]
+    lib.flce_profile_end.restype = c.c_int
+    return lib
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libflce.so (once).  torch is imported first so the library binds to
+    the HIP runtime torch already loaded (same soname)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise ImportError(
+                f"{path} is not built; run `python -m linear_cross_entropy_05_amd.build` (needs hipcc for gfx950)"
+            )
+        _lib = _declare(ctypes.CDLL(path))
+    return _lib
+
+
+def header_functions(header: str = HEADER) -> list[str]:
+    """Names of the functions include/flce.h declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_tensor(name, t, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+
+
+def flce_chunk_tokens(BT: int, H: int, V: int, chunk_tokens: int = 0, dtype=torch.bfloat16) -> int:
+    return int(load_library().flce_chunk_tokens(BT, H, V, chunk_tokens, _DTYPES[dtype]))
+
+
+def flce_workspace_bytes(BT: int, H: int, V: int, chunk_tokens: int = 0, dtype=torch.bfloat16) -> int:
+    return int(load_library().flce_workspace_bytes(BT, H, V, chunk_tokens, _DTYPES[dtype]))
+
+
+def ce_workspace_bytes(BT: int, V: int) -> int:
+    return int(load_library().ce_workspace_bytes(BT, V))
+
+
+def check_err_flag(err: torch.Tensor, what: str):
+    v = int(err.item())
+    if v != 0:
+        raise FlceError(v, what)
+
+
+def flce_fwd_bwd(X, W, targets, ignore_index: int = -100, chunk_tokens: int = 0, *, row_loss: bool = False,
+                 check: bool = True, out=None, workspace=None):
+    """Fused linear + cross-entropy forward and backward.
+
+    X [BT, H] and W [V, H] (fp32 or bf16, same dtype), targets [BT] int64.
+    Returns (loss fp32 0-d, dX [BT, H] X.dtype, dW [V, H] fp32) and, with
+    ``row_loss=True``, the per-token losses [BT] fp32.  With ``check`` the
+    call synchronises and raises if a target was out of range.  ``out`` may
+    pass preallocated (loss, dX, dW, err) tensors and ``workspace`` a uint8
+    device tensor, to keep allocations out of timed loops.
+    """
+    lib = load_library()
+    _check_tensor("X", X, ndim=2)
+    _check_tensor("W", W, dtype=X.dtype, ndim=2)
+    _check_tensor("targets", targets, dtype=torch.int64, ndim=1)
+    if X.dtype not in _DTYPES:
+        raise TypeError(f"dtype {X.dtype} not supported (float32, bfloat16)")
+    BT, H = X.shape
+    V = W.shape[0]
+    if W.shape[1] != H or targets.shape[0] != BT:
+        raise ValueError(f"shape mismatch X{tuple(X.shape)} W{tuple(W.shape)} targets{tuple(targets.shape)}")
+    dev = X.device
+    if out is None:
+        loss = torch.empty((), dtype=torch.float32, device=dev)
+        dX = torch.empty_like(X)
+        dW = torch.empty((V, H), dtype=torch.float32, device=dev)
+        err = torch.empty((1,), dtype=torch.int32, device=dev)
+    else:
+        loss, dX, dW, err = out
+    rl = torch.empty((BT,), dtype=torch.float32, device=dev) if row_loss else None
+    need = lib.flce_workspace_bytes(BT, H, V, chunk_tokens, _DTYPES[X.dtype])
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    st = lib.flce_fwd_bwd(
+        _ptr(X), _ptr(W), _ptr(targets), BT, H, V, ignore_index, chunk_tokens, _DTYPES[X.dtype], _ptr(loss),
+        _ptr(rl), _ptr(dX), _ptr(dW), _ptr(workspace), workspace.numel(), _ptr(err), _stream(dev))
+    if st != 0:
+        raise FlceError(st, "flce_fwd_bwd")
+    if check:
+        check_err_flag(err, "flce_fwd_bwd")
+    return (loss, dX, dW, rl) if row_loss else (loss, dX, dW)
+
+
+def ce_fwd_bwd_inplace(logits, targets, ignore_index: int = -100, *, row_loss: bool = False, check: bool = True):
+    """Cross-entropy on fp32 logits [BT, V]; overwrites logits with d loss / d logits.
+
+    Returns the fp32 loss (0-d) and, with ``row_loss=True``, per-token losses."""
+    lib = load_library()
+    _check_tensor("logits", logits, dtype=torch.float32, ndim=2)
+    _check_tensor("targets", targets, dtype=torch.int64, ndim=1)
+    BT, V = logits.shape
+    if targets.shape[0] != BT:
+        raise ValueError("targets length must equal logits rows")
+    dev = logits.device
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    err = torch.empty((1,), dtype=torch.int32, device=dev)
+    rl = torch.empty((BT,), dtype=torch.float32, device=dev) if row_loss else None
+    ws = torch.empty((lib.ce_workspace_bytes(BT, V),), dtype=torch.uint8, device=dev)
+    st = lib.ce_fwd_bwd_inplace(_ptr(logits), _ptr(targets), BT, V, ignore_index, _ptr(loss), _ptr(rl), _ptr(ws),
+                                ws.numel(), _ptr(err), _stream(dev))
+    if st != 0:
+        raise FlceError(st, "ce_fwd_bwd_inplace")
+    if check:
+        check_err_flag(err, "ce_fwd_bwd_inplace")
+    return (loss, rl) if row_loss else loss
+
+
+KERNEL_KINDS = ["count_valid", "logits", "lse", "grad_inplace", "dx", "dx_reduce", "dw", "loss_final",
+                "ce_rows", "fill_zero"]
+
+
+class KernelTimer:
+    """Per-kernel HIP-event timing of every library launch inside the block.
+
+        with KernelTimer() as kt:
+            ...calls...
+        kt.ms["logits"], kt.launches["logits"]
+    """
+
+    def __init__(self, max_launches: int = 65536):
+        self.max_launches = max_launches
+        self.ms = {}
+        self.launches = {}
+
+    def __enter__(self):
+        st = load_library().flce_profile_begin(self.max_launches)
+        if st != 0:
+            raise FlceError(st, "flce_profile_begin")
+        return self
+
+    def __exit__(self, *exc):
+        n = len(KERNEL_KINDS)
+        ms = (ctypes.c_double * n)()
+        cnt = (ctypes.c_int64 * n)()
+        st = load_library().flce_profile_end(ms, cnt, n)
+        self.ms = {k: ms[i] for i, k in enumerate(KERNEL_KINDS)}
+        self.launches = {k: cnt[i] for i, k in enumerate(KERNEL_KINDS)}
+        if st != 0 and exc[0] is None:
+            raise FlceError(st, "flce_profile_end")
+        return False
+
+
+class _FLCEFunction(torch.autograd.Function):
+    """Forward computes the loss and both gradients at once (one pass over the
+    chunks); backward scales the stored gradients by the upstream gradient."""
+
+    @staticmethod
+    def forward(ctx, weight, inp, target, ignore_index, chunk_tokens):
+        loss, dX, dW = flce_fwd_bwd(inp.contiguous(), weight.contiguous(), target.contiguous(), ignore_index,
+                                    chunk_tokens)
+        ctx.save_for_backward(dX, dW)
+        ctx.weight_dtype = weight.dtype
+        return loss
+
+    @staticmethod
+    def backward(ctx, grad):
+        dX, dW = ctx.saved_tensors
+        g = grad.to(torch.float32)
+        gx = (dX.float() * g).to(dX.dtype) if ctx.needs_input_grad[1] else None
+        gw = (dW * g).to(ctx.weight_dtype) if ctx.needs_input_grad[0] else None
+        return gw, gx, None, None, None
+
+
+class FusedLinearCrossEntropyLoss(torch.nn.Module):
+    """``loss = FusedLinearCrossEntropyLoss()(weight, input, target)``: mean
+    cross-entropy of ``input @ weight.T`` over targets != ignore_index."""
+
+    def __init__(self, ignore_index: int = -100, chunk_tokens: int = 0):
+        super().__init__()
+        self.ignore_index = ignore_index
+        self.chunk_tokens = chunk_tokens
+
+    def forward(self, weight, inp, target):
+        return _FLCEFunction.apply(weight, inp, target, self.ignore_index, self.chunk_tokens)

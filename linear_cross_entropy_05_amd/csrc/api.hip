@@ -1,0 +1,134 @@
+// C-ABI entry points: argument checks, workspace layout, and the token-chunk
+// schedule of fused linear + cross-entropy.
+//
+// Schedule of one flce_fwd_bwd call, all on the caller's stream:
+//   count N and check targets
+//   for each chunk of C tokens:  logits+statistics -> lse -> in-place grad
+//                                -> dX rows of the chunk -> dW (+)=
+//   loss = sum of token losses / N
+// Only one logits chunk exists at a time ("[論文レビュー] Liger Kernel:
+// Efficient Triton Kernels for LLM Training", 提案手法: chunked FLCE to bound
+// the memory of large-vocabulary logits).
+#include <string.h>
+
+#include "../../include/flce.h"
+#include "flce_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int device_status(int dev) {
+  if (dev < 0) return -1;
+  if (dev < kMaxDevices && g_device_ok[dev]) return g_device_ok[dev] == 1 ? 1 : 0;
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, dev) != hipSuccess) return -1;
+  const int ok = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+  if (dev < kMaxDevices) g_device_ok[dev] = ok ? 1 : 2;
+  return ok;
+}
+
+int current_device_ok() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  return device_status(dev);
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* flce_status_str(int status) {
+  switch (status) {
+    case FLCE_OK: return "ok";
+    case FLCE_ERR_ARG: return "invalid argument (null pointer or bad size)";
+    case FLCE_ERR_DTYPE: return "unsupported dtype";
+    case FLCE_ERR_WORKSPACE: return "workspace too small";
+    case FLCE_ERR_DEVICE: return "current device is not gfx950";
+    case FLCE_ERR_LAUNCH: return "kernel launch failed";
+    case FLCE_ERR_TARGET: return "target outside [0, V) that is not ignore_index";
+    case FLCE_ERR_SHAPE: return "unsupported shape (H must be a multiple of 8 for bf16, 4 for fp32)";
+    case FLCE_ERR_ALIGN: return "misaligned pointer";
+    default: return "unknown status";
+  }
+}
+
+int flce_device_supported(int device) { return device_status(device); }
+
+int64_t flce_chunk_tokens(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype) {
+  if (BT < 0 || H <= 0 || V <= 0 || (dtype != FLCE_F32 && dtype != FLCE_BF16)) return 0;
+  return flce::make_layout(BT, H, V, chunk_tokens, dtype).C;
+}
+
+size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype) {
+  if (BT < 0 || H <= 0 || V <= 0 || (dtype != FLCE_F32 && dtype != FLCE_BF16)) return 0;
+  return flce::make_layout(BT, H, V, chunk_tokens, dtype).total;
+}
+
+int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H, int64_t V,
+                 int64_t ignore_index, int64_t chunk_tokens, int dtype, float* loss, float* row_loss, void* dX,
+                 float* dW, void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream) {
+  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_ERR_DTYPE;
+  if (BT < 0 || H <= 0 || V <= 0 || BT > INT32_MAX || V > INT32_MAX) return FLCE_ERR_ARG;
+  if (!W || !loss || !dW || !workspace || !err_flag) return FLCE_ERR_ARG;
+  if (BT > 0 && (!X || !targets || !dX)) return FLCE_ERR_ARG;
+  if (H % (dtype == FLCE_BF16 ? 8 : 4) != 0) return FLCE_ERR_SHAPE;
+  if (!aligned(W, 16) || (X && !aligned(X, 16)) || (targets && !aligned(targets, 8)) || !aligned(workspace, 256) ||
+      !aligned(dW, 4) || (dX && !aligned(dX, dtype == FLCE_BF16 ? 2 : 4)) || (row_loss && !aligned(row_loss, 4)))
+    return FLCE_ERR_ALIGN;
+  const flce::Layout L = flce::make_layout(BT, H, V, chunk_tokens, dtype);
+  if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE;
+  if (current_device_ok() != 1) return FLCE_ERR_DEVICE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* nvalid = reinterpret_cast<int32_t*>(ws + L.off_nvalid);
+  float* rl = row_loss ? row_loss : reinterpret_cast<float*>(ws + L.off_rowloss);
+
+  if (flce::launch_count_valid(targets, BT, V, ignore_index, nvalid, err_flag, s) != hipSuccess)
+    return FLCE_ERR_LAUNCH;
+  if (BT == 0) {
+    if (flce::launch_fill_zero(dW, V * H, s) != hipSuccess) return FLCE_ERR_LAUNCH;
+  }
+  for (int64_t c0 = 0; c0 < BT; c0 += L.C) {
+    const int64_t rows = BT - c0 < L.C ? BT - c0 : L.C;
+    if (flce::launch_flce_chunk(L, X, W, targets, ignore_index, c0, rows, ws, rl, dX, dW, c0 == 0, s) != hipSuccess)
+      return FLCE_ERR_LAUNCH;
+  }
+  if (flce::launch_loss_final(rl, BT, nvalid, loss, s) != hipSuccess) return FLCE_ERR_LAUNCH;
+  return FLCE_OK;
+}
+
+size_t ce_workspace_bytes(int64_t BT, int64_t V) {
+  if (BT < 0 || V <= 0) return 0;
+  return 256 + (((size_t)(BT > 0 ? BT : 1) * 4 + 255) & ~(size_t)255);
+}
+
+int ce_fwd_bwd_inplace(float* logits, const int64_t* targets, int64_t BT, int64_t V, int64_t ignore_index,
+                       float* loss, float* row_loss, void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                       void* stream) {
+  if (BT < 0 || V <= 0 || BT > INT32_MAX) return FLCE_ERR_ARG;
+  if (!loss || !workspace || !err_flag) return FLCE_ERR_ARG;
+  if (BT > 0 && (!logits || !targets)) return FLCE_ERR_ARG;
+  if ((logits && !aligned(logits, 4)) || (targets && !aligned(targets, 8)) || !aligned(workspace, 256) ||
+      (row_loss && !aligned(row_loss, 4)))
+    return FLCE_ERR_ALIGN;
+  if (workspace_bytes < ce_workspace_bytes(BT, V)) return FLCE_ERR_WORKSPACE;
+  if (current_device_ok() != 1) return FLCE_ERR_DEVICE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* nvalid = reinterpret_cast<int32_t*>(ws);
+  float* rl = row_loss ? row_loss : reinterpret_cast<float*>(ws + 256);
+  if (flce::launch_count_valid(targets, BT, V, ignore_index, nvalid, err_flag, s) != hipSuccess)
+    return FLCE_ERR_LAUNCH;
+  if (flce::launch_ce_rows(logits, targets, BT, V, ignore_index, nvalid, rl, s) != hipSuccess)
+    return FLCE_ERR_LAUNCH;
+  if (flce::launch_loss_final(rl, BT, nvalid, loss, s) != hipSuccess) return FLCE_ERR_LAUNCH;
+  return FLCE_OK;
+}
+
+}  // extern "C"

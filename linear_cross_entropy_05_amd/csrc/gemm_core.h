@@ -1,0 +1,326 @@
+// MFMA tile GEMM building blocks for gfx950 (CDNA4), shared by the three
+// contractions of fused linear + cross-entropy:
+//   logits   Z^T[v,c] = sum_h W[v,h] X[c,h]     (both operands K-contiguous)
+//   dX       dX[c,h]  = sum_v G[c,v] W[v,h]     (W read K-major: transposed)
+//   dW       dW[v,h] += sum_c G[c,v] X[c,h]     (both read K-major: transposed)
+//
+// A workgroup of 256 threads (4 wave64s, 2 x 2) owns a 256 x 256 output tile;
+// each wave owns 128 x 128 = 4 x 4 MFMA 32x32 blocks (16 fp32 accumulators
+// per lane per block).  K advances 128 bytes per stage (64 bf16 or 32 fp32),
+// double-buffered in LDS: 2 stages x 2 operands x 32 KiB = 128 KiB of the
+// 160 KiB gfx950 LDS.
+//
+// LDS holds every operand "row-major in K": tile row r (an M or N index) is
+// 128 bytes of consecutive K, split into eight 16-byte chunks.  Chunk c of row
+// r sits at slot (c ^ r ^ (r >> 3)) & 7, which keeps both the row-wise MFMA
+// fragment reads and the transposing writes free of bank conflicts.
+//
+// Operands stored K-contiguous in HBM are copied chunk by chunk.  Operands
+// stored K-major (MN contiguous) are loaded as 8 x 8 (bf16) or 4 x 4 (fp32)
+// element blocks, one 16-byte load per K row, transposed in registers and
+// written as K-contiguous chunks.
+//
+// MFMA operand mapping: for v_mfma_f32_32x32x16_bf16 lane l feeds row
+// (l % 32) of its operand with the 8 K values of chunk (2 s + l / 32) of the
+// current stage (s = 0..3).  A and B use the same K assignment, so the
+// contraction is exact whatever order the hardware sums the K slots in.  The
+// fp32 path issues four v_mfma_f32_32x32x2f32 per chunk pair, element t of
+// each lane's chunk feeding the t-th instruction.  Accumulator element e of
+// lane l is output row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace flce {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kTile = 256;                      // output tile edge (M and N)
+constexpr int kThreads = 256;                   // 4 waves
+constexpr int kRowBytes = 128;                  // K bytes per tile row per stage
+constexpr int kOpBytes = kTile * kRowBytes;     // one operand, one stage: 32 KiB
+constexpr int kStageBytes = 2 * kOpBytes;       // A + B
+constexpr int kLdsBytes = 2 * kStageBytes;      // double buffered: 128 KiB
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<__bf16> {
+  static constexpr int chunk = 8;               // elements per 16-byte chunk
+};
+template <>
+struct Elem<float> {
+  static constexpr int chunk = 4;
+};
+template <typename T>
+constexpr int kStageK = kRowBytes / (int)sizeof(T);  // K elements per stage
+
+// One GEMM operand as it lies in HBM.  For a K-contiguous operand, memory
+// rows are M (or N) indices and memory columns are K; for a K-major one the
+// other way round.  `rows` bounds the memory rows that may be read; `cols`
+// bounds the K extent of a K-contiguous operand (chunks starting at or past
+// it read as zero).  Reads past the operand's last valid element return zero
+// (buffer range checking); other reads past `cols` in a K-major operand land
+// on M/N indices whose outputs are never stored.
+template <typename T>
+struct Operand {
+  const T* base;
+  int64_t ld;    // elements between consecutive memory rows
+  int64_t rows;  // valid memory rows
+  int64_t cols;  // valid memory columns
+};
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+// Buffer resource over [base, base + bytes): loads at or past `bytes` read 0,
+// stores there are dropped.  Only byte offsets below 2^31 are ever used.
+// Callers pass workgroup-uniform values; readfirstlane makes that explicit so
+// the resource always lives in scalar registers.
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const int nn = __builtin_amdgcn_readfirstlane((int)n);
+  void* q = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, nn, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload16(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+__device__ __forceinline__ uint32_t lds_off(uint32_t r, uint32_t c) {
+  return r * kRowBytes + (((c ^ r ^ (r >> 3)) & 7u) << 4);
+}
+
+// ---- global -> registers -------------------------------------------------
+
+// K-contiguous operand, view of one 256-row tile: thread t loads chunk t % 8
+// of rows t / 8 + 32 i (i = 0..7) at each stage.
+template <typename T>
+struct KContigLoader {
+  Rsrc r;
+  uint32_t voff;     // this thread's byte offset within the tile
+  uint32_t row32;    // bytes between rows t / 8 + 32 i and + 32 (i + 1)
+  int64_t kchunk;    // this thread's K offset within a stage (elements)
+  int64_t kend;      // K bound
+
+  __device__ __forceinline__ void init(const Operand<T>& op, int64_t mn0, int tid) {
+    const int64_t nrows = op.rows - mn0 < kTile ? op.rows - mn0 : kTile;
+    r = make_rsrc(op.base + mn0 * op.ld, nrows * op.ld * (int64_t)sizeof(T));
+    voff = (uint32_t)(((tid >> 3) * op.ld + (tid & 7) * Elem<T>::chunk) * (int64_t)sizeof(T));
+    row32 = (uint32_t)(32 * op.ld * (int64_t)sizeof(T));
+    kchunk = (tid & 7) * Elem<T>::chunk;
+    kend = op.cols;
+  }
+  __device__ __forceinline__ void load(u32x4 (&st)[8], int64_t k0) const {
+    const uint32_t soff = (uint32_t)(k0 * (int64_t)sizeof(T));
+    const bool ok = k0 + kchunk < kend;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4 v = bload16(r, voff + i * row32, soff);
+      st[i] = ok ? v : u32x4{0, 0, 0, 0};
+    }
+  }
+};
+
+// K-major operand.  bf16: thread t loads the 8 x 8 block at K rows
+// 8 (t / 32) + j, MN columns 8 (t % 32) ..; fp32: the 4 x 4 blocks at K rows
+// 4 (t / 64 + 4 i) + j, MN columns 4 (t % 64) .. (i = 0, 1).  The resource is
+// rebuilt per stage from (k0, mn0), so offsets stay within one stage.
+template <typename T>
+struct KMajorLoader {
+  const T* base;
+  int64_t ld, rows, cols, mn0;
+  uint32_t voff;
+
+  __device__ __forceinline__ void init(const Operand<T>& op, int64_t mn0_, int tid) {
+    base = op.base;
+    ld = op.ld;
+    rows = op.rows;
+    cols = op.cols;
+    mn0 = mn0_;
+    if constexpr (sizeof(T) == 2)
+      voff = (uint32_t)((8 * (tid >> 5) * ld + 8 * (tid & 31)) * (int64_t)sizeof(T));
+    else
+      voff = (uint32_t)((4 * (tid >> 6) * ld + 4 * (tid & 63)) * (int64_t)sizeof(T));
+  }
+  __device__ __forceinline__ void load(u32x4 (&st)[8], int64_t k0) const {
+    // valid bytes from (k0, mn0) to the end of the last valid row's columns
+    const int64_t nb = rows > k0 ? ((rows - k0 - 1) * ld + (cols - mn0)) * (int64_t)sizeof(T) : 0;
+    const Rsrc r = make_rsrc(base + k0 * ld + mn0, nb);
+    const uint32_t rowb = (uint32_t)(ld * (int64_t)sizeof(T));
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) st[j] = bload16(r, voff, j * rowb);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st[4 * i + j] = bload16(r, voff, (16 * i + j) * rowb);
+    }
+  }
+};
+
+// ---- registers -> LDS ------------------------------------------------------
+
+__device__ __forceinline__ void store_kcontig(char* lds, const u32x4 (&st)[8], int tid) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = tid + kThreads * i;
+    *reinterpret_cast<u32x4*>(lds + lds_off(q >> 3, q & 7)) = st[i];
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_kmajor(char* lds, const u32x4 (&st)[8], int tid);
+
+// 8 x 8 bf16 transpose: st[j] holds K row j, MN columns 0..7 (two per dword).
+// Output row p (MN column p) gets K values 0..7 packed two per dword.
+template <>
+__device__ __forceinline__ void store_kmajor<__bf16>(char* lds, const u32x4 (&st)[8], int tid) {
+  const int mc = tid & 31, kb = tid >> 5;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = st[2 * q][p >> 1], hi = st[2 * q + 1][p >> 1];
+      o[q] = (p & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+    *reinterpret_cast<u32x4*>(lds + lds_off(mc * 8 + p, kb)) = o;
+  }
+}
+
+template <>
+__device__ __forceinline__ void store_kmajor<float>(char* lds, const u32x4 (&st)[8], int tid) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int b = tid + kThreads * i;
+    const int mc = b & 63, kb = b >> 6;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const u32x4 o = {st[4 * i][p], st[4 * i + 1][p], st[4 * i + 2][p], st[4 * i + 3][p]};
+      *reinterpret_cast<u32x4*>(lds + lds_off(mc * 4 + p, kb)) = o;
+    }
+  }
+}
+
+// ---- MFMA on one stage -------------------------------------------------------
+
+template <typename T>
+__device__ __forceinline__ f32x16 mma_chunk(u32x4 a, u32x4 b, f32x16 c);
+
+template <>
+__device__ __forceinline__ f32x16 mma_chunk<__bf16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ f32x16 mma_chunk<float>(u32x4 a, u32x4 b, f32x16 c) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a[t]), __builtin_bit_cast(float, b[t]), c,
+                                             0, 0, 0);
+  return c;
+}
+
+template <typename T>
+__device__ __forceinline__ void mma_stage(const char* ldsA, const char* ldsB, f32x16 (&acc)[4][4], int wy,
+                                          int wx, int lane) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int c = 2 * s + (lane >> 5);
+    u32x4 a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const u32x4*>(ldsA + lds_off(wy * 128 + 32 * i + (lane & 31), c));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const u32x4*>(ldsB + lds_off(wx * 128 + 32 * j + (lane & 31), c));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mma_chunk<T>(a[i], b[j], acc[i][j]);
+  }
+}
+
+// ---- the main loop -----------------------------------------------------------
+
+template <typename T, bool kKMajor>
+__device__ __forceinline__ void store_op(char* lds, const u32x4 (&st)[8], int tid) {
+  if constexpr (kKMajor)
+    store_kmajor<T>(lds, st, tid);
+  else
+    store_kcontig(lds, st, tid);
+}
+
+template <typename T, bool kKMajor>
+using LoaderOf = typename std::conditional<kKMajor, KMajorLoader<T>, KContigLoader<T>>::type;
+
+// acc = A[m0:m0+256, k0:k1] * B[n0:n0+256, k0:k1]^T.  The stages cover
+// [k0, k0 + KS * ceil((k1 - k0) / KS)); the caller makes the K extent past
+// k1 read as zero (operand bounds) or lets it land on zero padding.
+template <typename T, bool kAKMajor, bool kBKMajor>
+__device__ __forceinline__ void gemm_mainloop(char* smem, const Operand<T>& A, int64_t m0, const Operand<T>& B,
+                                              int64_t n0, int64_t k0, int64_t k1, f32x16 (&acc)[4][4]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wy = wave >> 1, wx = wave & 1;
+  constexpr int KS = kStageK<T>;
+  const int nk = (int)((k1 - k0 + KS - 1) / KS);
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  if (nk <= 0) return;
+
+  LoaderOf<T, kAKMajor> la;
+  LoaderOf<T, kBKMajor> lb;
+  la.init(A, m0, tid);
+  lb.init(B, n0, tid);
+  u32x4 sa[8], sb[8];
+  la.load(sa, k0);
+  lb.load(sb, k0);
+  store_op<T, kAKMajor>(smem, sa, tid);
+  store_op<T, kBKMajor>(smem + kOpBytes, sb, tid);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    char* cur = smem + (kt & 1) * kStageBytes;
+    char* nxt = smem + ((kt + 1) & 1) * kStageBytes;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      const int64_t kn = k0 + (int64_t)(kt + 1) * KS;
+      la.load(sa, kn);
+      lb.load(sb, kn);
+    }
+    mma_stage<T>(cur, cur + kOpBytes, acc, wy, wx, lane);
+    if (more) {
+      store_op<T, kAKMajor>(nxt, sa, tid);
+      store_op<T, kBKMajor>(nxt + kOpBytes, sb, tid);
+    }
+    __syncthreads();
+  }
+}
+
+// Map a linear workgroup id onto a tile id so that each XCD (workgroups are
+// dealt round-robin over 8 of them) walks one contiguous range of tile ids:
+// neighbouring tiles share an operand block, which then stays in that XCD's L2.
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t total) {
+  constexpr int64_t kXcds = 8;
+  const int64_t x = b % kXcds, k = b / kXcds;
+  const int64_t q = total / kXcds, r = total % kXcds;
+  return x * q + (x < r ? x : r) + k;
+}
+
+}  // namespace flce

@@ -1,6 +1,7 @@
 """Float64 CPU oracle for FLCE (test infrastructure only; never on the product path)."""
 from .flce_oracle import (  # noqa: F401
     ce_ref,
+    ce_rows_ref,
     check_targets,
     flce_brute_force,
     flce_ref,

@@ -84,6 +84,7 @@ def check_targets(y, V: int, ignore_index: int = -100) -> None:
 
 def row_lse(Z: np.ndarray) -> np.ndarray:
     """Row-wise log-sum-exp, shifted by the row maximum for range safety."""
+    Z = _as_f64(Z)
     m = Z.max(axis=1, keepdims=True)
     return (m + np.log(np.exp(Z - m).sum(axis=1, keepdims=True)))[:, 0]
 
@@ -97,24 +98,51 @@ def ce_ref(logits, y, ignore_index: int = -100):
     kernel leaves in the logits buffer), ``row_loss`` [BT] (0 on ignored rows),
     ``lse`` [BT] and ``n_valid``.
     """
-    Z = _as_f64(logits)
+    return _ce(np.array(_as_f64(logits), dtype=np.float64, copy=True), y, ignore_index)
+
+
+def _ce(Z: np.ndarray, y, ignore_index: int, n_valid=None):
+    """ce_ref on a float64 logits array it overwrites (Z becomes dlogits).
+
+    ``n_valid`` overrides N (the count of non-ignored rows) when Z holds only
+    some rows of a larger batch.
+    """
     y = _as_i64(y)
     BT, V = Z.shape
     check_targets(y, V, ignore_index)
     keep = y != ignore_index
-    n = int(keep.sum())
+    n = int(keep.sum()) if n_valid is None else int(n_valid)
     denom = float(max(n, 1))
-    lse = row_lse(Z) if BT else np.zeros(0)
     rows = np.arange(BT)
-    yy = np.where(keep, y, 0)
-    z_target = Z[rows, yy] if BT else np.zeros(0)
+    z_target = Z[rows, np.where(keep, y, 0)].copy()
+    # log-sum-exp shifted by the row maximum: Z <- exp(Z - m), s = row sums
+    m = Z.max(axis=1) if BT else np.zeros(0)
+    Z -= m[:, None]
+    np.exp(Z, out=Z)
+    s = Z.sum(axis=1)
+    lse = m + np.log(s)
     row_loss = np.where(keep, lse - z_target, 0.0)
     loss = float(row_loss.sum() / denom)
-    P = np.exp(Z - lse[:, None]) if BT else Z.copy()
-    P[rows[keep], y[keep]] -= 1.0
-    P[~keep, :] = 0.0
-    G = P / denom
-    return {"loss": loss, "dlogits": G, "row_loss": row_loss, "lse": lse, "n_valid": n}
+    # softmax = exp(Z - m) / s; minus the one-hot target; over N; ignored rows 0
+    Z /= s[:, None]
+    Z[rows[keep], y[keep]] -= 1.0
+    Z[~keep, :] = 0.0
+    Z /= denom
+    return {"loss": loss, "dlogits": Z, "row_loss": row_loss, "lse": lse, "n_valid": n}
+
+
+def ce_rows_ref(logits_rows, y_rows, n_valid: int, ignore_index: int = -100):
+    """ce_ref for a subset of rows of a larger batch whose N is ``n_valid``.
+
+    Every row's loss term and gradient depend only on that row and on N, so
+    selected rows can be checked one by one at sizes where the whole batch is
+    too large for the CPU.  Returns ``row_loss``, ``lse`` and ``dlogits`` of
+    those rows (the latter divided by the batch's N).
+    """
+    Z = np.array(_as_f64(logits_rows), dtype=np.float64, copy=True)
+    out = _ce(Z, y_rows, ignore_index, n_valid=n_valid)
+    out.pop("loss")
+    return out
 
 
 def flce_ref(X, W, y, ignore_index: int = -100):
@@ -129,7 +157,7 @@ def flce_ref(X, W, y, ignore_index: int = -100):
     if X64.ndim != 2 or W64.ndim != 2 or X64.shape[1] != W64.shape[1]:
         raise ValueError(f"shape mismatch X{X64.shape} W{W64.shape}")
     Z = X64 @ W64.T
-    out = ce_ref(Z, y, ignore_index)
+    out = _ce(Z, y, ignore_index)  # Z is overwritten by dlogits
     G = out["dlogits"]
     out["dX"] = G @ W64
     out["dW"] = G.T @ X64

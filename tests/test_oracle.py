@@ -84,3 +84,20 @@ def test_oracle_upcasts_bf16_exactly():
     z = np.array([(1 + 2 ** -7) * 0.5 - 0.75, (1 + 2 ** -7) * 2 ** -9 - 3.0])
     lse = z.max() + math.log(np.exp(z - z.max()).sum())
     assert out["loss"] == pytest.approx(lse - z[1], rel=1e-15)
+
+
+def test_ce_rows_ref_matches_full_batch():
+    r = np.random.default_rng(6)
+    Z = r.standard_normal((12, 40)) * 3
+    y = r.integers(0, 40, 12)
+    y[[2, 5]] = -100
+    full = oracle.ce_ref(Z, y)
+    rows = [0, 2, 7, 11]
+    part = oracle.ce_rows_ref(Z[rows], y[rows], n_valid=full["n_valid"])
+    assert np.allclose(part["row_loss"], full["row_loss"][rows], rtol=1e-14, atol=0)
+    assert np.allclose(part["dlogits"], full["dlogits"][rows], rtol=1e-13, atol=1e-18)
+
+
+def test_row_lse_closed_form():
+    Z = np.log(np.array([[1.0, 2.0, 3.0, 4.0], [0.5, 0.5, 0.5, 0.5]]))
+    assert np.allclose(oracle.row_lse(Z), [np.log(10.0), np.log(2.0)], rtol=1e-15)
