@@ -228,10 +228,11 @@ __device__ __forceinline__ f32x16 mma_chunk<__bf16>(u32x4 a, u32x4 b, f32x16 c) 
 
 template <>
 __device__ __forceinline__ f32x16 mma_chunk<float>(u32x4 a, u32x4 b, f32x16 c) {
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a[t]), __builtin_bit_cast(float, b[t]), c,
-                                             0, 0, 0);
+  const f32x4 af = __builtin_bit_cast(f32x4, a), bf = __builtin_bit_cast(f32x4, b);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(af.x, bf.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(af.y, bf.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(af.z, bf.z, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(af.w, bf.w, c, 0, 0, 0);
   return c;
 }
 

@@ -8,13 +8,14 @@
 // logits buffer is overwritten by d(loss)/d(logits); the computation is exact.
 // Per chunk of `rows` tokens (c indexes the chunk's tokens, v the vocabulary,
 // h the hidden units):
-//   logits   Z[c,v] = x_c . w_v, stored to the chunk buffer; per (token,
-//            256-wide vocabulary tile) the running max m and sum of
-//            exp(z - m), and the target's logit, taken from the fp32
-//            accumulators in the GEMM epilogue
+//   logits   Z[c,v] = x_c . w_v; per (token, 256-wide vocabulary tile t)
+//            the max M_t and sum of exp(z - M_t), and the target's logit,
+//            taken from the fp32 accumulators in the GEMM epilogue; the
+//            chunk buffer receives z - M_t in the element type
 //   lse      lse_c = M + ln sum_t s_t e^(m_t - M) over the tiles, M = max m_t;
 //            per-token loss lse_c - z_{c,y_c} (0 for ignored tokens)
-//   grad     G[c,v] = (e^(Z[c,v] - lse_c) - [v = y_c]) / N written over Z
+//   grad     G[c,v] = (e^(Z[c,v] - lse_c) - [v = y_c]) / N written over the
+//            stored z - M_t
 //            (0 on ignored tokens), N = number of non-ignored tokens
 //   dX       dX[c,:] = G[c,:] W
 //   dW       dW (+)= G^T X_chunk, fp32, stored on the first chunk
@@ -126,7 +127,9 @@ __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
   const int64_t cw = c0 + wx * 128 + (lane & 31);
   const bool full = v0 + kTile <= a.V;
 
-  float mj[4], sj[4];
+  // 1. per token: the max over this wave's 128 vocabulary entries (in-lane
+  //    over 64 values, then with the lane holding the other 64)
+  float mj[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float m = -FLT_MAX;
@@ -135,19 +138,9 @@ __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         if (full || vw + 32 * i + 8 * (e >> 2) + (e & 3) < a.V) m = fmaxf(m, acc[i][j][e]);
-    m = fmaxf(m, __shfl_xor(m, 32));
-    const float mb = m * kLog2e;
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (full || vw + 32 * i + 8 * (e >> 2) + (e & 3) < a.V) s += exp2_fast(fmaf(acc[i][j][e], kLog2e, -mb));
-    s += __shfl_xor(s, 32);
-    mj[j] = m;
-    sj[j] = s;
+    mj[j] = fmaxf(m, __shfl_xor(m, 32));
 
-    // the target logit, from the one lane that holds it
+    // the target logit, from the one lane that holds it (fp32, before rounding)
     const int64_t c = cw + 32 * j;
     if (c < a.rows) {
       const int64_t t = a.y[c] - (v0 + wy * 128);
@@ -162,12 +155,47 @@ __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
     }
   }
 
-  // combine the two waves that share these tokens (wy = 0, 1) through LDS;
-  // the main loop ended on a barrier, so the stage buffers are free
-  float2* xch = reinterpret_cast<float2*>(smem);
-  if (wy == 1 && lane < 32) {
+  // 2. the tile max M over both waves that hold these tokens (wy = 0, 1),
+  //    through LDS; the main loop ended on a barrier, so LDS is free
+  float* xm = reinterpret_cast<float*>(smem);        // [2][256] wave maxima
+  float* xs = xm + 2 * kTile;                        // [2][256] wave sums
+  if (lane < 32) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xch[wx * 128 + 32 * j + lane] = float2{mj[j], sj[j]};
+    for (int j = 0; j < 4; ++j) xm[wy * kTile + wx * 128 + 32 * j + lane] = mj[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) mj[j] = fmaxf(mj[j], xm[(wy ^ 1) * kTile + wx * 128 + 32 * j + (lane & 31)]);
+
+  // 3. sum of exp(z - M) over the tile, and z - M rounded to the chunk's
+  //    element type: stored relative to the tile max, the entries that carry
+  //    most of the softmax mass are small numbers and keep their precision.
+  //    Rows are padded to a multiple of 256, so a tile never crosses into the
+  //    next row; entries past V fill the padding (zeroed later).
+  const int64_t nrows = a.rows - c0 < kTile ? a.rows - c0 : kTile;
+  const Rsrc zr = make_rsrc(a.z + c0 * a.ldz, nrows * a.ldz * (int64_t)sizeof(T));
+  const uint32_t lane_off = (uint32_t)(((wx * 128 + (lane & 31)) * a.ldz + vw) * (int64_t)sizeof(T));
+  const uint32_t row32 = (uint32_t)(32 * a.ldz * (int64_t)sizeof(T));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float M = mj[j];
+    const float mb = M * kLog2e;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (full || vw + 32 * i + 8 * (e >> 2) + (e & 3) < a.V) s += exp2_fast(fmaf(acc[i][j][e], kLog2e, -mb));
+    s += __shfl_xor(s, 32);
+    if (lane < 32) xs[wy * kTile + wx * 128 + 32 * j + lane] = s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& q = acc[i][j];
+        store4(zr, lane_off + j * row32 + (uint32_t)((32 * i + 8 * g) * (int64_t)sizeof(T)), q[4 * g] - M,
+               q[4 * g + 1] - M, q[4 * g + 2] - M, q[4 * g + 3] - M, (T*)nullptr);
+      }
   }
   __syncthreads();
   if (wy == 0 && lane < 32) {
@@ -175,33 +203,10 @@ __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
     for (int j = 0; j < 4; ++j) {
       const int64_t c = cw + 32 * j;
       if (c < a.rows) {
-        const float2 o = xch[wx * 128 + 32 * j + lane];
-        const float M = fmaxf(mj[j], o.x);
-        const float S = sj[j] * exp2_fast((mj[j] - M) * kLog2e) + o.y * exp2_fast((o.x - M) * kLog2e);
-        a.part[c * a.nvt + vt] = float2{M, S};
+        const int k = wx * 128 + 32 * j + lane;
+        a.part[c * a.nvt + vt] = float2{mj[j], xs[k] + xs[kTile + k]};
       }
     }
-  }
-
-  // the logits themselves, rounded to the chunk's element type.  Rows are
-  // padded to a multiple of 256, so a tile never crosses into the next row;
-  // entries past V are 0 (W rows past V read as zero) and fill the padding.
-  {
-    const int64_t nrows = a.rows - c0 < kTile ? a.rows - c0 : kTile;
-    const Rsrc zr = make_rsrc(a.z + c0 * a.ldz, nrows * a.ldz * (int64_t)sizeof(T));
-    const uint32_t lane_off =
-        (uint32_t)(((wx * 128 + (lane & 31)) * a.ldz + vw) * (int64_t)sizeof(T));
-    const uint32_t row32 = (uint32_t)(32 * a.ldz * (int64_t)sizeof(T));
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x16& q = acc[i][j];
-          store4(zr, lane_off + j * row32 + (uint32_t)((32 * i + 8 * g) * (int64_t)sizeof(T)), q[4 * g], q[4 * g + 1],
-                 q[4 * g + 2], q[4 * g + 3], (T*)nullptr);
-        }
   }
 }
 
@@ -237,10 +242,13 @@ __device__ __forceinline__ float grad1(float z, float lb, int64_t v, int64_t t, 
   return v < V ? (exp2_fast(fmaf(z, kLog2e, -lb)) - (v == t ? 1.f : 0.f)) * inv : 0.f;
 }
 
+// The chunk holds z - M_t (M_t: max of the token's vocabulary tile t), so the
+// probability is exp(stored + M_t - lse).
 template <typename T>
 __global__ __launch_bounds__(256) void k_grad(T* __restrict__ z, int64_t ldz, int64_t V,
-                                              const float* __restrict__ lse, const int64_t* __restrict__ y,
-                                              int64_t ign, const int32_t* __restrict__ nvalid) {
+                                              const float* __restrict__ lse, const float2* __restrict__ part,
+                                              int64_t nvt, const int64_t* __restrict__ y, int64_t ign,
+                                              const int32_t* __restrict__ nvalid) {
   constexpr int E = Elem<T>::chunk;
   const int64_t c = blockIdx.x;
   const int64_t t = y[c];
@@ -252,9 +260,12 @@ __global__ __launch_bounds__(256) void k_grad(T* __restrict__ z, int64_t ldz, in
   }
   const int n = *nvalid;
   const float inv = 1.f / (float)(n > 0 ? n : 1);
-  const float lb = lse[c] * kLog2e;
+  const float l = lse[c];
+  const float2* pc = part + c * nvt;
   for (int64_t v = (int64_t)threadIdx.x * E; v < ldz; v += 256 * E) {
     u32x4 d = *reinterpret_cast<const u32x4*>(row + v);
+    const int64_t tile = v / kTile;
+    const float lb = (l - (tile < nvt ? pc[tile].x : 0.f)) * kLog2e;
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -265,9 +276,10 @@ __global__ __launch_bounds__(256) void k_grad(T* __restrict__ z, int64_t ldz, in
         d[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){g0, g1}, bf16x2));
       }
     } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        d[q] = __builtin_bit_cast(uint32_t, grad1(__builtin_bit_cast(float, d[q]), lb, v + q, t, V, inv));
+      const f32x4 zf = __builtin_bit_cast(f32x4, d);
+      const f32x4 g = {grad1(zf.x, lb, v, t, V, inv), grad1(zf.y, lb, v + 1, t, V, inv),
+                       grad1(zf.z, lb, v + 2, t, V, inv), grad1(zf.w, lb, v + 3, t, V, inv)};
+      d = __builtin_bit_cast(u32x4, g);
     }
     *reinterpret_cast<u32x4*>(row + v) = d;
   }
@@ -529,7 +541,8 @@ static hipError_t chunk_impl(const Layout& L, const T* X, const T* W, const int6
   }
   {
     ProfScope ps(kPhaseGrad, s);
-    hipLaunchKernelGGL(k_grad<T>, dim3((unsigned)rows), dim3(256), 0, s, z, L.ldz, V, lse, yc, ign, nvalid);
+    hipLaunchKernelGGL(k_grad<T>, dim3((unsigned)rows), dim3(256), 0, s, z, L.ldz, V, lse, part, L.nvt, yc, ign,
+                       nvalid);
   }
 
   // dX = G W
