@@ -99,6 +99,42 @@ def gpu_bench(w, steps, warmup):
             "cus": props.multi_processor_count, "arch": getattr(props, "gcnArchName", "?")}
 
 
+def copy_calibration(nbytes=256 << 20, reps=3):
+    """A plain device-to-device copy of known size, so that profiler byte
+    counters (FETCH_SIZE, WRITE_SIZE) can be scaled against it."""
+    import torch
+
+    dev = torch.device("cuda", 0)
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {reps} x {nbytes} bytes read + written")
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (profiles/hbm_traffic.json), or None if the kernel sources changed
+    since the counters were taken (hash of linear_cross_entropy_05_amd/csrc)."""
+    import glob
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "linear_cross_entropy_05_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    if h.hexdigest()[:16] != t.get("source_sha256"):
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return int(k["bytes_per_launch"]) if k else None
+
+
 def roofline(w, r):
     """Dominant kernel (largest time per step) against its own roofline."""
     name, k = max(r["kernels"].items(), key=lambda kv: kv[1]["ms_per_step"])
@@ -118,17 +154,15 @@ def roofline(w, r):
     if name in per_launch_flops:
         achieved = per_launch_flops[name] / (k["avg_ms"] * 1e-3) / 1e12
         return name, {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(name)}
     achieved = per_launch_bytes.get(name, 0.0) / (k["avg_ms"] * 1e-3) / 1e9
     return name, {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                  "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+                  "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(name)}
 
 
 def cpu_baseline(w, sample_tokens):
     """The float64 oracle on the host cores, on the first `sample_tokens` tokens
     of the same workload (full W), as tokens/s."""
-    import numpy as np
-
     import oracle
     import synth_inputs as si
 
@@ -159,6 +193,8 @@ def main(argv=None):
     ap.add_argument("--config", default="llama3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); this build has no multi-GPU path.",
@@ -168,6 +204,8 @@ def main(argv=None):
     import synth_inputs as si
 
     w = si.workload(a.config)
+    if a.copy_calibration:
+        copy_calibration()
     r = gpu_bench(w, a.steps, a.warmup)
     tokens_per_s = w.BT / (r["ms"] * 1e-3)
     tflops = 6.0 * w.BT * w.H * w.V / (r["ms"] * 1e-3) / 1e12
