@@ -16,10 +16,10 @@ struct Layout {
   int dtype;        // 0 fp32, 1 bf16
   int64_t C;        // tokens per chunk
   int64_t ldz;      // elements between chunk rows (V rounded up to 256)
-  int64_t nvt;      // vocabulary tiles of the logits GEMM (ceil(V / 256))
+  int64_t nvt;      // vocabulary tiles of the logits GEMM (ceil(V / 256)); statistics per half tile
   int64_t splits;   // K splits of the dX GEMM
   int64_t esize;    // bytes per element of X, W and the chunk
-  size_t off_nvalid, off_zt, off_lse, off_rowloss, off_part, off_chunk, off_dxpart, total;
+  size_t off_nvalid, off_lse, off_rowloss, off_part, off_chunk, off_dxpart, total;
 };
 
 Layout make_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);

@@ -124,12 +124,10 @@ struct KContigLoader {
   }
   __device__ __forceinline__ void load(u32x4 (&st)[8], int64_t k0) const {
     const uint32_t soff = (uint32_t)(k0 * (int64_t)sizeof(T));
-    const bool ok = k0 + kchunk < kend;
+    // chunks past the K bound: an offset past every resource's range reads 0
+    const uint32_t v = k0 + kchunk < kend ? voff : 0x80000000u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const u32x4 v = bload16(r, voff + i * row32, soff);
-      st[i] = ok ? v : u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < 8; ++i) st[i] = bload16(r, v + i * row32, soff);
   }
 };
 
@@ -236,21 +234,29 @@ __device__ __forceinline__ f32x16 mma_chunk<float>(u32x4 a, u32x4 b, f32x16 c) {
   return c;
 }
 
+// One stage = 4 steps of 16 bf16 (8 fp32) K values.  The fragments of step
+// s + 1 are read from LDS while the 16 MFMAs of step s run.
+__device__ __forceinline__ void read_frags(const char* ldsA, const char* ldsB, u32x4 (&a)[4], u32x4 (&b)[4], int wy,
+                                           int wx, int lane, int s) {
+  const int c = 2 * s + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const u32x4*>(ldsA + lds_off(wy * 128 + 32 * i + (lane & 31), c));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const u32x4*>(ldsB + lds_off(wx * 128 + 32 * j + (lane & 31), c));
+}
+
 template <typename T>
 __device__ __forceinline__ void mma_stage(const char* ldsA, const char* ldsB, f32x16 (&acc)[4][4], int wy,
                                           int wx, int lane) {
+  u32x4 a[2][4], b[2][4];
+  read_frags(ldsA, ldsB, a[0], b[0], wy, wx, lane, 0);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const int c = 2 * s + (lane >> 5);
-    u32x4 a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const u32x4*>(ldsA + lds_off(wy * 128 + 32 * i + (lane & 31), c));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const u32x4*>(ldsB + lds_off(wx * 128 + 32 * j + (lane & 31), c));
+    if (s < 3) read_frags(ldsA, ldsB, a[(s + 1) & 1], b[(s + 1) & 1], wy, wx, lane, s + 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mma_chunk<T>(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = mma_chunk<T>(a[s & 1][i], b[s & 1][j], acc[i][j]);
   }
 }
 
@@ -271,7 +277,7 @@ using LoaderOf = typename std::conditional<kKMajor, KMajorLoader<T>, KContigLoad
 // [k0, k0 + KS * ceil((k1 - k0) / KS)); the caller makes the K extent past
 // k1 read as zero (operand bounds) or lets it land on zero padding.
 template <typename T, bool kAKMajor, bool kBKMajor>
-__device__ __forceinline__ void gemm_mainloop(char* smem, const Operand<T>& A, int64_t m0, const Operand<T>& B,
+__device__ __forceinline__ void mainloop_regstage(char* smem, const Operand<T>& A, int64_t m0, const Operand<T>& B,
                                               int64_t n0, int64_t k0, int64_t k1, f32x16 (&acc)[4][4]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -312,6 +318,278 @@ __device__ __forceinline__ void gemm_mainloop(char* smem, const Operand<T>& A, i
     }
     __syncthreads();
   }
+}
+
+// ---- bf16 pipelined main loop -------------------------------------------------
+//
+// Global -> LDS copies go straight into LDS (buffer_load ... lds, 16 bytes per
+// lane; a wave's instruction fills 1 KiB of LDS in lane order), NS stages of
+// 32 bf16 of K deep, so loads for stage k + NS - 1 are in flight while stage k
+// is multiplied.  Tiles in LDS:
+//   K-contiguous operand: 256 rows x 64 bytes; 16-byte chunk c of row r at
+//     slot c ^ ((r >> 1) ^ (r >> 3)) & 3 (the copying lane picks the chunk
+//     that belongs at its slot).  Fragments: ds_read_b128.
+//   K-major operand: 32 K rows x 512 bytes (256 MN values); 32-byte segment
+//     s of K row k at position s ^ {0, 2, 5, 7}[k % 4].  Fragments: two
+//     ds_read_b64_tr_b16, which hand lane i of each 16-lane group element t
+//     of the 8 bytes read by lane 4 t + i / 4 of that group (so lane 4 t + q
+//     points at K row t, MN columns 4 q .. 4 q + 3, and lane i receives MN
+//     column i for four consecutive K rows).
+// Both swizzles keep fragment reads free of LDS bank conflicts.
+// Each stage has one barrier, placed between its two 16-MFMA steps so the
+// MFMAs already issued cover the wait and the next stage's first fragment
+// reads overlap the second step.
+namespace pipe {
+
+constexpr int kBK = 32;           // bf16 K per stage
+constexpr int kRowB = 64;         // bytes per K-contiguous tile row per stage
+constexpr int kOp = 256 * kRowB;  // 16 KiB per operand per stage
+constexpr int kStage = 2 * kOp;   // 32 KiB
+constexpr int kLoads = 4;         // 1 KiB copies per wave per operand per stage
+
+typedef __attribute__((address_space(3))) void* lds_void;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t kc_off(uint32_t r, uint32_t c) {
+  return r * kRowB + (((c ^ (r >> 1) ^ (r >> 3)) & 3u) << 4);
+}
+__device__ __forceinline__ uint32_t km_sw(uint32_t k) { return (0x7520u >> (4 * (k & 3u))) & 15u; }
+__device__ __forceinline__ uint32_t km_off(uint32_t k, uint32_t n) {
+  return k * 512u + ((((n >> 4) ^ km_sw(k)) & 15u) << 5) + ((n & 15u) << 1);
+}
+
+// Buffer resource as four scalar words (for the inline-asm copies below).
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, int64_t bytes) {
+  const int64_t n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : bytes);
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) & 0xffffu;
+  const uint32_t nr = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)n);
+  return u32x4{lo, hi, nr, 0x00020000u};
+}
+
+// 16 bytes per lane from the buffer straight into LDS at lds + 16 * lane.
+// Written as inline asm so that the compiler does not add its own
+// conservative "wait for every outstanding load" before later LDS reads: the
+// pipeline places the waits itself (wait_vm), also in inline asm.
+__device__ __forceinline__ void dma16(u32x4 r, const char* lds, uint32_t voff, uint32_t soff) {
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(r), "s"(soff)
+               : "memory", "m0");
+}
+
+// K-contiguous operand, one 256-row tile.  Copy q of wave w fills rows
+// 16 g .. 16 g + 15 (g = w + 4 q); lane i fills row 16 g + i / 4, slot i % 4.
+struct KcLoader {
+  u32x4 r;
+  uint32_t voff[kLoads];
+  uint32_t kch[kLoads];  // K offset (elements) of the chunk each copy reads
+  int64_t kend;
+  __device__ __forceinline__ void init(const Operand<__bf16>& op, int64_t mn0, int wave, int lane) {
+    const int64_t nrows = op.rows - mn0 < kTile ? op.rows - mn0 : kTile;
+    r = rsrc_words(op.base + mn0 * op.ld, nrows * op.ld * 2);
+    kend = op.cols;
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+      const uint32_t row = 16 * (wave + 4 * q) + (lane >> 2);
+      const uint32_t c = ((lane & 3) ^ (row >> 1) ^ (row >> 3)) & 3u;
+      kch[q] = 8 * c;
+      voff[q] = (uint32_t)((row * op.ld + 8 * c) * 2);
+    }
+  }
+  struct Stage {
+    bool tail;
+    int64_t k0;
+  };
+  __device__ __forceinline__ Stage prep(int64_t k0) const { return Stage{k0 + kBK > kend, k0}; }
+  __device__ __forceinline__ void issue_one(const Stage& st, const char* tile, int q, int wave) const {
+    const uint32_t v = (!st.tail || st.k0 + kch[q] < kend) ? voff[q] : 0x80000000u;
+    dma16(r, tile + 1024 * (wave + 4 * q), v, (uint32_t)(st.k0 * 2));
+  }
+  __device__ __forceinline__ void issue(const char* tile, int64_t k0, int wave) const {
+    const Stage st = prep(k0);
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) issue_one(st, tile, q, wave);
+  }
+  __device__ __forceinline__ u32x4 frag(const char* tile, int row, int c) const {
+    return *reinterpret_cast<const u32x4*>(tile + kc_off(row, c));
+  }
+};
+
+// K-major operand (memory rows are K): copy q of wave w fills K rows 2 g and
+// 2 g + 1 (g = w + 4 q); lane i fills K row 2 g + i / 32, 16 bytes at
+// position (i % 32) / 2, half i % 2.
+struct KmLoader {
+  const __bf16* base;
+  int64_t ld, rows, cols, mn0;
+  uint32_t voff[kLoads];
+  __device__ __forceinline__ void init(const Operand<__bf16>& op, int64_t mn0_, int wave, int lane) {
+    base = op.base;
+    ld = op.ld;
+    rows = op.rows;
+    cols = op.cols;
+    mn0 = mn0_;
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+      const uint32_t k = 2 * (wave + 4 * q) + (lane >> 5);
+      const uint32_t seg = (((lane & 31) >> 1) ^ km_sw(k)) & 15u;
+      voff[q] = (uint32_t)((k * ld + 16 * seg + 8 * (lane & 1)) * 2);
+    }
+  }
+  struct Stage {
+    u32x4 r;
+  };
+  __device__ __forceinline__ Stage prep(int64_t k0) const {
+    const int64_t nb = rows > k0 ? ((rows - k0 - 1) * ld + (cols - mn0)) * 2 : 0;
+    return Stage{rsrc_words(base + k0 * ld + mn0, nb)};
+  }
+  __device__ __forceinline__ void issue_one(const Stage& st, const char* tile, int q, int wave) const {
+    dma16(st.r, tile + 1024 * (wave + 4 * q), voff[q], 0);
+  }
+  __device__ __forceinline__ void issue(const char* tile, int64_t k0, int wave) const {
+    const Stage st = prep(k0);
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) issue_one(st, tile, q, wave);
+  }
+  // fragment of MN columns nb .. nb + 31, K rows 16 s + 8 (lane / 32) .. + 7
+  __device__ __forceinline__ u32x4 frag(const char* tile, int nb, int s, int lane) const {
+    const uint32_t g = lane >> 4, q = lane & 3, t = (lane >> 2) & 3;
+    const uint32_t n = nb + 16 * (g & 1) + 4 * q;
+    const uint32_t k = 16 * s + 8 * (g >> 1) + t;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(tile + km_off(k, n)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(tile + km_off(k + 4, n)));
+    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+    return u32x4{a.x, a.y, b.x, b.y};
+  }
+};
+
+template <bool kKMajor>
+using LoaderT = typename std::conditional<kKMajor, KmLoader, KcLoader>::type;
+
+template <bool kKMajor>
+__device__ __forceinline__ u32x4 read_frag(const LoaderT<kKMajor>& l, const char* tile, int rb, int s, int lane) {
+  if constexpr (kKMajor)
+    return l.frag(tile, rb, s, lane);
+  else
+    return l.frag(tile, rb + (lane & 31), 2 * s + (lane >> 5));
+}
+
+// s_waitcnt vmcnt(N): at most N of this wave's copies still in flight
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// wait until at most n (0..3) stages of this wave's copies are in flight
+__device__ __forceinline__ void wait_stages(int n) {
+  constexpr int L = 2 * kLoads;
+  if (n <= 0)
+    wait_vm<0>();
+  else if (n == 1)
+    wait_vm<L>();
+  else if (n == 2)
+    wait_vm<2 * L>();
+  else
+    wait_vm<3 * L>();
+}
+
+template <bool kAKMajor, bool kBKMajor, int NS>
+__device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, int64_t m0, const Operand<__bf16>& B,
+                                         int64_t n0, int64_t k0, int64_t k1, f32x16 (&acc)[4][4]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wy = wave >> 1, wx = wave & 1;
+  const int nk = (int)((k1 - k0 + kBK - 1) / kBK);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  if (nk <= 0) return;
+
+  LoaderT<kAKMajor> la;
+  LoaderT<kBKMajor> lb;
+  la.init(A, m0, wave, lane);
+  lb.init(B, n0, wave, lane);
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk) {
+      la.issue(smem + st * kStage, k0 + (int64_t)st * kBK, wave);
+      lb.issue(smem + st * kStage + kOp, k0 + (int64_t)st * kBK, wave);
+    }
+  wait_stages(nk - 1 < NS - 2 ? nk - 1 : NS - 2);
+  __syncthreads();
+
+  u32x4 fa[2][4], fb[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[0][i] = read_frag<kAKMajor>(la, smem, wy * 128 + 32 * i, 0, lane);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fb[0][j] = read_frag<kBKMajor>(lb, smem + kOp, wx * 128 + 32 * j, 0, lane);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* cur = smem + (kt % NS) * kStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[1][i] = read_frag<kAKMajor>(la, cur, wy * 128 + 32 * i, 1, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[1][j] = read_frag<kBKMajor>(lb, cur + kOp, wx * 128 + 32 * j, 1, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mma_chunk<__bf16>(fa[0][i], fb[0][j], acc[i][j]);
+    if (kt + 1 < nk) {
+      // stage kt + 1 landed (this wave's copies), then everyone's; buffer
+      // (kt - 1) % NS is no longer read by anyone
+      const int ahead = nk - 2 - kt;
+      wait_stages(ahead < NS - 3 ? ahead : NS - 3);
+      __syncthreads();
+      if (kt + NS - 1 < nk) {
+        char* dst = smem + ((kt + NS - 1) % NS) * kStage;
+        la.issue(dst, k0 + (int64_t)(kt + NS - 1) * kBK, wave);
+        lb.issue(dst + kOp, k0 + (int64_t)(kt + NS - 1) * kBK, wave);
+      }
+      const char* nxt = smem + ((kt + 1) % NS) * kStage;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[0][i] = read_frag<kAKMajor>(la, nxt, wy * 128 + 32 * i, 0, lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[0][j] = read_frag<kBKMajor>(lb, nxt + kOp, wx * 128 + 32 * j, 0, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mma_chunk<__bf16>(fa[1][i], fb[1][j], acc[i][j]);
+  }
+  __syncthreads();  // LDS free for the epilogue
+}
+
+}  // namespace pipe
+
+// acc = A[m0:m0+256, k0:k1) * B[n0:n0+256, k0:k1)^T: the direct-to-LDS
+// pipeline for bf16, the register-staged loop for fp32.
+constexpr int kPipeStages = 4;
+
+template <typename T, bool kAKMajor, bool kBKMajor>
+__device__ __forceinline__ void gemm_mainloop(char* smem, const Operand<T>& A, int64_t m0, const Operand<T>& B,
+                                              int64_t n0, int64_t k0, int64_t k1, f32x16 (&acc)[4][4]) {
+  if constexpr (sizeof(T) == 2)
+    pipe::mainloop<kAKMajor, kBKMajor, kPipeStages>(smem, A, m0, B, n0, k0, k1, acc);
+  else
+    mainloop_regstage<T, kAKMajor, kBKMajor>(smem, A, m0, B, n0, k0, k1, acc);
+}
+
+// Tile (tm, tn) of a tm-count x tn-count grid for tile id t, walking groups
+// of `group` consecutive tm rows column by column: concurrently running tiles
+// then share few A row-blocks and few B column-blocks (L2 reuse).
+__device__ __forceinline__ void grouped_tile(int64_t t, int64_t ntm, int64_t ntn, int64_t group, int64_t& tm,
+                                             int64_t& tn) {
+  const int64_t per_group = group * ntn;
+  const int64_t g = t / per_group;
+  const int64_t first = g * group;
+  const int64_t rows = ntm - first < group ? ntm - first : group;
+  const int64_t l = t - g * per_group;
+  tm = first + l % rows;
+  tn = l / rows;
 }
 
 // Map a linear workgroup id onto a tile id so that each XCD (workgroups are

@@ -8,14 +8,15 @@
 // logits buffer is overwritten by d(loss)/d(logits); the computation is exact.
 // Per chunk of `rows` tokens (c indexes the chunk's tokens, v the vocabulary,
 // h the hidden units):
-//   logits   Z[c,v] = x_c . w_v; per (token, 256-wide vocabulary tile t)
-//            the max M_t and sum of exp(z - M_t), and the target's logit,
-//            taken from the fp32 accumulators in the GEMM epilogue; the
-//            chunk buffer receives z - M_t in the element type
-//   lse      lse_c = M + ln sum_t s_t e^(m_t - M) over the tiles, M = max m_t;
+//   logits   Z[c,v] = x_c . w_v; per (token, 128-wide vocabulary half tile h)
+//            the max M_h and sum of exp(z - M_h), taken from the fp32
+//            accumulators in the GEMM epilogue; the chunk buffer receives
+//            z - M_h in the element type
+//   lse      lse_c = M + ln sum_h s_h e^(M_h - M) over the half tiles,
+//            M = max M_h; target logit x_c . w_y (fp32 dot product);
 //            per-token loss lse_c - z_{c,y_c} (0 for ignored tokens)
 //   grad     G[c,v] = (e^(Z[c,v] - lse_c) - [v = y_c]) / N written over the
-//            stored z - M_t
+//            stored z - M_h
 //            (0 on ignored tokens), N = number of non-ignored tokens
 //   dX       dX[c,:] = G[c,:] W
 //   dW       dW (+)= G^T X_chunk, fp32, stored on the first chunk
@@ -88,11 +89,10 @@ template <typename T>
 struct LogitsArgs {
   Operand<T> W;  // A: [V, H], K = H contiguous
   Operand<T> X;  // B: chunk tokens [rows, H]
-  const int64_t* y;
   int64_t V, H, rows, nvt, nct, ldz;
+  int64_t nvh;     // 128-wide vocabulary half tiles: 2 nvt
   T* z;            // chunk buffer [rows, ldz]
-  float2* part;    // [rows, nvt] (max, sum of exp) per vocabulary tile
-  float* zt;       // [rows] target logit
+  float2* part;    // [rows, nvh] (max, sum of exp) per half tile
 };
 
 __device__ __forceinline__ void store4(Rsrc r, uint32_t off, float a, float b, float c, float d, __bf16*) {
@@ -109,11 +109,20 @@ __device__ __forceinline__ void store4(Rsrc r, uint32_t off, float a, float b, f
       r, (int)off, 0, 0);
 }
 
+__device__ __forceinline__ void store4_ptr(__bf16* p, float a, float b, float c, float d) {
+  const bf16x2 lo = __builtin_convertvector((f32x2){a, b}, bf16x2);
+  const bf16x2 hi = __builtin_convertvector((f32x2){c, d}, bf16x2);
+  *reinterpret_cast<uint2*>(p) = uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+__device__ __forceinline__ void store4_ptr(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
-  const int64_t tile = xcd_tile(blockIdx.x, a.nvt * a.nct);
-  const int64_t vt = tile / a.nct, ct = tile % a.nct;
+  int64_t vt, ct;
+  grouped_tile(xcd_tile(blockIdx.x, a.nvt * a.nct), a.nvt, a.nct, 4, vt, ct);
   const int64_t v0 = vt * kTile, c0 = ct * kTile;
 
   f32x16 acc[4][4];
@@ -123,116 +132,103 @@ __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
   const int wy = wave >> 1, wx = wave & 1;
   // accumulator (i, j, e) holds Z[c, v] with
   //   v = vw + 32 i + 8 (e / 4) + e % 4,  c = cw + 32 j + lane % 32
+  // Each wave covers 128 vocabulary entries (a half tile h = 2 vt + wy) of
+  // 128 tokens; its statistics are its own, so no data is exchanged.
   const int64_t vw = v0 + wy * 128 + 4 * (lane >> 5);
   const int64_t cw = c0 + wx * 128 + (lane & 31);
-  const bool full = v0 + kTile <= a.V;
-
-  // 1. per token: the max over this wave's 128 vocabulary entries (in-lane
-  //    over 64 values, then with the lane holding the other 64)
-  float mj[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float m = -FLT_MAX;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (full || vw + 32 * i + 8 * (e >> 2) + (e & 3) < a.V) m = fmaxf(m, acc[i][j][e]);
-    mj[j] = fmaxf(m, __shfl_xor(m, 32));
-
-    // the target logit, from the one lane that holds it (fp32, before rounding)
-    const int64_t c = cw + 32 * j;
-    if (c < a.rows) {
-      const int64_t t = a.y[c] - (v0 + wy * 128);
-      if (t >= 0 && t < 128 && ((t >> 2) & 1) == (lane >> 5)) {
-        const int i = (int)(t >> 5), g = (int)((t >> 3) & 3), r = (int)(t & 3);
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (ii == i && (e >> 2) == g && (e & 3) == r) a.zt[c] = acc[ii][j][e];
-      }
-    }
-  }
-
-  // 2. the tile max M over both waves that hold these tokens (wy = 0, 1),
-  //    through LDS; the main loop ended on a barrier, so LDS is free
-  float* xm = reinterpret_cast<float*>(smem);        // [2][256] wave maxima
-  float* xs = xm + 2 * kTile;                        // [2][256] wave sums
-  if (lane < 32) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xm[wy * kTile + wx * 128 + 32 * j + lane] = mj[j];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 4; ++j) mj[j] = fmaxf(mj[j], xm[(wy ^ 1) * kTile + wx * 128 + 32 * j + (lane & 31)]);
-
-  // 3. sum of exp(z - M) over the tile, and z - M rounded to the chunk's
-  //    element type: stored relative to the tile max, the entries that carry
-  //    most of the softmax mass are small numbers and keep their precision.
-  //    Rows are padded to a multiple of 256, so a tile never crosses into the
-  //    next row; entries past V fill the padding (zeroed later).
+  const bool full = v0 + wy * 128 + 128 <= a.V;
+  const int64_t half = 2 * vt + wy;
   const int64_t nrows = a.rows - c0 < kTile ? a.rows - c0 : kTile;
   const Rsrc zr = make_rsrc(a.z + c0 * a.ldz, nrows * a.ldz * (int64_t)sizeof(T));
   const uint32_t lane_off = (uint32_t)(((wx * 128 + (lane & 31)) * a.ldz + vw) * (int64_t)sizeof(T));
   const uint32_t row32 = (uint32_t)(32 * a.ldz * (int64_t)sizeof(T));
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float M = mj[j];
-    const float mb = M * kLog2e;
-    float s = 0.f;
+    // max over the 128 entries of token c: 64 in this lane, 64 in lane ^ 32
+    float m = -FLT_MAX;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        if (full || vw + 32 * i + 8 * (e >> 2) + (e & 3) < a.V) s += exp2_fast(fmaf(acc[i][j][e], kLog2e, -mb));
-    s += __shfl_xor(s, 32);
-    if (lane < 32) xs[wy * kTile + wx * 128 + 32 * j + lane] = s;
+        if (full || vw + 32 * i + 8 * (e >> 2) + (e & 3) < a.V) m = fmaxf(m, acc[i][j][e]);
+    m = fmaxf(m, __shfl_xor(m, 32));
+    const float mb = m * kLog2e;
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (full || vw + 32 * i + 8 * (e >> 2) + (e & 3) < a.V) sum += exp2_fast(fmaf(acc[i][j][e], kLog2e, -mb));
+    sum += __shfl_xor(sum, 32);
+    const int64_t c = cw + 32 * j;
+    if (lane < 32 && c < a.rows) a.part[c * a.nvh + half] = float2{m, sum};
+    // z - m, rounded to the chunk's element type: the entries that carry
+    // most of the softmax mass are then small numbers and keep their
+    // precision.  Rows are padded to a multiple of 256, so a tile never
+    // crosses into the next row; entries past V fill the padding.
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x16& q = acc[i][j];
-        store4(zr, lane_off + j * row32 + (uint32_t)((32 * i + 8 * g) * (int64_t)sizeof(T)), q[4 * g] - M,
-               q[4 * g + 1] - M, q[4 * g + 2] - M, q[4 * g + 3] - M, (T*)nullptr);
+        store4(zr, lane_off + j * row32 + (uint32_t)((32 * i + 8 * g) * (int64_t)sizeof(T)), q[4 * g] - m,
+               q[4 * g + 1] - m, q[4 * g + 2] - m, q[4 * g + 3] - m, (T*)nullptr);
       }
-  }
-  __syncthreads();
-  if (wy == 0 && lane < 32) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t c = cw + 32 * j;
-      if (c < a.rows) {
-        const int k = wx * 128 + 32 * j + lane;
-        a.part[c * a.nvt + vt] = float2{mj[j], xs[k] + xs[kTile + k]};
-      }
-    }
   }
 }
 
 // ---- log-sum-exp over the vocabulary tiles, per-token loss --------------------
 
-__global__ __launch_bounds__(256) void k_lse(const float2* __restrict__ part, int64_t nvt,
-                                             const float* __restrict__ zt, const int64_t* __restrict__ y,
-                                             int64_t ign, int64_t rows, float* __restrict__ lse,
-                                             float* __restrict__ rowloss) {
+// One wave per token: combine the half-tile statistics into lse, and take the
+// target's logit as the dot product x_c . w_y in fp32 (the same products the
+// MFMA accumulates, summed in a different order).
+template <typename T>
+__global__ __launch_bounds__(256) void k_lse(const float2* __restrict__ part, int64_t nvh, const T* __restrict__ X,
+                                             const T* __restrict__ W, int64_t H, int64_t V,
+                                             const int64_t* __restrict__ y, int64_t ign, int64_t rows,
+                                             float* __restrict__ lse, float* __restrict__ rowloss) {
+  constexpr int E = Elem<T>::chunk;
   const int lane = threadIdx.x & 63;
   const int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (c >= rows) return;
-  const float2* p = part + c * nvt;
+  const float2* p = part + c * nvh;
   float M = -FLT_MAX;
-  for (int64_t t = lane; t < nvt; t += 64) M = fmaxf(M, p[t].x);
+  for (int64_t t = lane; t < nvh; t += 64) M = fmaxf(M, p[t].x);
   M = wave_max(M);
   float S = 0.f;
-  for (int64_t t = lane; t < nvt; t += 64) {
+  for (int64_t t = lane; t < nvh; t += 64) {
     const float2 q = p[t];
     S += q.y * exp2_fast((q.x - M) * kLog2e);
   }
   S = wave_sum(S);
+  const int64_t t = y[c];
+  float zt = 0.f;
+  if (t != ign && t >= 0 && t < V) {
+    const T* xr = X + c * H;
+    const T* wr = W + t * H;
+    for (int64_t h = (int64_t)lane * E; h < H; h += 64 * E) {
+      const u32x4 xa = *reinterpret_cast<const u32x4*>(xr + h);
+      const u32x4 wa = *reinterpret_cast<const u32x4*>(wr + h);
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          zt = fmaf(__builtin_bit_cast(float, xa[q] << 16), __builtin_bit_cast(float, wa[q] << 16), zt);
+          zt = fmaf(__builtin_bit_cast(float, xa[q] & 0xffff0000u), __builtin_bit_cast(float, wa[q] & 0xffff0000u), zt);
+        }
+      } else {
+        const f32x4 xf = __builtin_bit_cast(f32x4, xa), wf = __builtin_bit_cast(f32x4, wa);
+        zt = fmaf(xf.x, wf.x, zt);
+        zt = fmaf(xf.y, wf.y, zt);
+        zt = fmaf(xf.z, wf.z, zt);
+        zt = fmaf(xf.w, wf.w, zt);
+      }
+    }
+  }
+  zt = wave_sum(zt);
   if (lane == 0) {
     const float l = M + logf(S);
     lse[c] = l;
-    rowloss[c] = (y[c] != ign) ? l - zt[c] : 0.f;
+    rowloss[c] = (t != ign) ? l - zt : 0.f;
   }
 }
 
@@ -242,12 +238,12 @@ __device__ __forceinline__ float grad1(float z, float lb, int64_t v, int64_t t, 
   return v < V ? (exp2_fast(fmaf(z, kLog2e, -lb)) - (v == t ? 1.f : 0.f)) * inv : 0.f;
 }
 
-// The chunk holds z - M_t (M_t: max of the token's vocabulary tile t), so the
-// probability is exp(stored + M_t - lse).
+// The chunk holds z - M_h (M_h: max of the token's 128-wide vocabulary half
+// tile h), so the probability is exp(stored + M_h - lse).
 template <typename T>
 __global__ __launch_bounds__(256) void k_grad(T* __restrict__ z, int64_t ldz, int64_t V,
                                               const float* __restrict__ lse, const float2* __restrict__ part,
-                                              int64_t nvt, const int64_t* __restrict__ y, int64_t ign,
+                                              int64_t nvh, const int64_t* __restrict__ y, int64_t ign,
                                               const int32_t* __restrict__ nvalid) {
   constexpr int E = Elem<T>::chunk;
   const int64_t c = blockIdx.x;
@@ -261,11 +257,11 @@ __global__ __launch_bounds__(256) void k_grad(T* __restrict__ z, int64_t ldz, in
   const int n = *nvalid;
   const float inv = 1.f / (float)(n > 0 ? n : 1);
   const float l = lse[c];
-  const float2* pc = part + c * nvt;
+  const float2* pc = part + c * nvh;
   for (int64_t v = (int64_t)threadIdx.x * E; v < ldz; v += 256 * E) {
     u32x4 d = *reinterpret_cast<const u32x4*>(row + v);
-    const int64_t tile = v / kTile;
-    const float lb = (l - (tile < nvt ? pc[tile].x : 0.f)) * kLog2e;
+    const int64_t h = v / 128;
+    const float lb = (l - (h < nvh ? pc[h].x : 0.f)) * kLog2e;
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -289,8 +285,8 @@ __global__ __launch_bounds__(256) void k_grad(T* __restrict__ z, int64_t ldz, in
 
 template <typename T>
 struct DxArgs {
-  Operand<T> G;  // A: chunk buffer [rows, ldz], K = V contiguous
-  Operand<T> W;  // B: [V, H] read K-major
+  Operand<T> G;  // chunk buffer [rows, ldz], K = V contiguous: the GEMM's B (columns c)
+  Operand<T> W;  // [V, H] read K-major: the GEMM's A (rows h)
   int64_t V, H, rows, nmt, nnt, ksplit;
   T* dx;         // [rows, H] when not split
   float* part;   // [splits, rows, H] when split
@@ -308,14 +304,15 @@ __global__ __launch_bounds__(256) void k_dx(DxArgs<T> a) {
   if (k1 < G.cols) G.cols = k1;
   if (k1 < W.rows) W.rows = k1;
 
+  // W^T as the A operand (rows h) and G as B (columns c): each lane then
+  // holds four consecutive h of one dX row
   f32x16 acc[4][4];
-  gemm_mainloop<T, false, true>(smem, G, m0, W, n0, k0, k1, acc);
+  gemm_mainloop<T, true, false>(smem, W, n0, G, m0, k0, k1, acc);
 
-  // accumulator (i, j, e) holds output row m0 + mw + 32 i + 8 (e / 4) + e % 4,
-  // column n0 + nw + 32 j; offsets are taken from the tile's first row
+  // accumulator (i, j, e): h = n0 + hw + 32 i + 8 (e / 4) + e % 4, c = m0 + cw + 32 j
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int mw = (wave >> 1) * 128 + 4 * (lane >> 5);
-  const int nw = (wave & 1) * 128 + (lane & 31);
+  const int hw = (wave >> 1) * 128 + 4 * (lane >> 5);
+  const int cw = (wave & 1) * 128 + (lane & 31);
   const int mlim = (int)(a.rows - m0 < kTile ? a.rows - m0 : kTile);
   const int nlim = (int)(a.H - n0 < kTile ? a.H - n0 : kTile);
   const bool split = gridDim.y > 1;
@@ -325,19 +322,20 @@ __global__ __launch_bounds__(256) void k_dx(DxArgs<T> a) {
   const bool full = mlim == kTile && nlim == kTile;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int n = nw + 32 * j;
-    if (!full && n >= nlim) continue;
+    const int c = cw + 32 * j;
+    if (!full && c >= mlim) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = mw + 32 * i + 8 * (e >> 2) + (e & 3);
-        if (full || m < mlim) {
-          const uint32_t off = (uint32_t)m * H + (uint32_t)n;
+      for (int g = 0; g < 4; ++g) {
+        const int h = hw + 32 * i + 8 * g;
+        if (full || h < nlim) {
+          const uint32_t off = (uint32_t)c * H + (uint32_t)h;
+          const f32x16& q = acc[i][j];
           if (split)
-            pbase[off] = acc[i][j][e];
+            *reinterpret_cast<f32x4*>(pbase + off) = f32x4{q[4 * g], q[4 * g + 1], q[4 * g + 2], q[4 * g + 3]};
           else
-            dbase[off] = (T)acc[i][j][e];
+            store4_ptr(dbase + off, q[4 * g], q[4 * g + 1], q[4 * g + 2], q[4 * g + 3]);
         }
       }
   }
@@ -357,8 +355,8 @@ __global__ __launch_bounds__(256) void k_dx_reduce(const float* __restrict__ par
 
 template <typename T>
 struct DwArgs {
-  Operand<T> G;  // A: chunk buffer read K-major ([rows = K][ldz = M])
-  Operand<T> X;  // B: chunk tokens [rows = K][H = N], read K-major
+  Operand<T> G;  // chunk buffer read K-major ([rows = K][ldz]): the GEMM's B (columns v)
+  Operand<T> X;  // chunk tokens [rows = K][H], read K-major: the GEMM's A (rows h)
   int64_t V, H, rows, nvt, nht;
   float* dw;     // [V, H]
   int first;
@@ -367,16 +365,19 @@ struct DwArgs {
 template <typename T>
 __global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
-  const int64_t tile = xcd_tile(blockIdx.x, a.nvt * a.nht);
-  const int64_t vt = tile / a.nht, ht = tile % a.nht;
+  int64_t vt, ht;
+  grouped_tile(xcd_tile(blockIdx.x, a.nvt * a.nht), a.nvt, a.nht, 4, vt, ht);
   const int64_t v0 = vt * kTile, h0 = ht * kTile;
 
+  // X_chunk^T as the A operand (rows h) and G^T as B (columns v): each lane
+  // then holds four consecutive h of one dW row, one 16-byte access each
   f32x16 acc[4][4];
-  gemm_mainloop<T, true, true>(smem, a.G, v0, a.X, h0, 0, a.rows, acc);
+  gemm_mainloop<T, true, true>(smem, a.X, h0, a.G, v0, 0, a.rows, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int vw = (wave >> 1) * 128 + 4 * (lane >> 5);
-  const int hw = (wave & 1) * 128 + (lane & 31);
+  // accumulator (i, j, e): h = h0 + hw + 32 i + 8 (e / 4) + e % 4, v = v0 + vw + 32 j
+  const int hw = (wave >> 1) * 128 + 4 * (lane >> 5);
+  const int vw = (wave & 1) * 128 + (lane & 31);
   const int vlim = (int)(a.V - v0 < kTile ? a.V - v0 : kTile);
   const int hlim = (int)(a.H - h0 < kTile ? a.H - h0 : kTile);
   float* base = a.dw + v0 * a.H + h0;
@@ -384,16 +385,17 @@ __global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
   const bool full = vlim == kTile && hlim == kTile;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int h = hw + 32 * j;
-    if (!full && h >= hlim) continue;
+    const int v = vw + 32 * j;
+    if (!full && v >= vlim) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int v = vw + 32 * i + 8 * (e >> 2) + (e & 3);
-        if (full || v < vlim) {
-          float* p = base + ((uint32_t)v * H + (uint32_t)h);
-          *p = a.first ? acc[i][j][e] : *p + acc[i][j][e];
+      for (int g = 0; g < 4; ++g) {
+        const int h = hw + 32 * i + 8 * g;
+        if (full || h < hlim) {
+          f32x4* p = reinterpret_cast<f32x4*>(base + ((uint32_t)v * H + (uint32_t)h));
+          const f32x4 r = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          *p = a.first ? r : *p + r;
         }
       }
   }
@@ -465,14 +467,12 @@ Layout make_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int d
   size_t o = 0;
   L.off_nvalid = o;
   o = align256(o + 16);
-  L.off_zt = o;
-  o = align256(o + (size_t)C * 4);
   L.off_lse = o;
   o = align256(o + (size_t)C * 4);
   L.off_rowloss = o;
   o = align256(o + (size_t)(BT > 0 ? BT : 1) * 4);
   L.off_part = o;
-  o = align256(o + (size_t)C * L.nvt * 8);
+  o = align256(o + (size_t)C * 2 * L.nvt * 8);
   L.off_chunk = o;
   o = align256(o + chunk_bytes);
   L.off_dxpart = o;
@@ -509,7 +509,6 @@ static hipError_t chunk_impl(const Layout& L, const T* X, const T* W, const int6
   const int64_t H = L.H, V = L.V;
   T* z = reinterpret_cast<T*>(ws + L.off_chunk);
   float2* part = reinterpret_cast<float2*>(ws + L.off_part);
-  float* zt = reinterpret_cast<float*>(ws + L.off_zt);
   float* lse = reinterpret_cast<float*>(ws + L.off_lse);
   const int32_t* nvalid = reinterpret_cast<const int32_t*>(ws + L.off_nvalid);
   const T* Xc = X + c0 * H;
@@ -519,16 +518,15 @@ static hipError_t chunk_impl(const Layout& L, const T* X, const T* W, const int6
   LogitsArgs<T> la;
   la.W = Operand<T>{W, H, V, H};
   la.X = Operand<T>{Xc, H, rows, H};
-  la.y = yc;
   la.V = V;
   la.H = H;
   la.rows = rows;
   la.nvt = L.nvt;
+  la.nvh = 2 * L.nvt;
   la.nct = (rows + kTile - 1) / kTile;
   la.ldz = L.ldz;
   la.z = z;
   la.part = part;
-  la.zt = zt;
   {
     ProfScope ps(kPhaseLogits, s);
     hipLaunchKernelGGL(k_logits<T>, dim3((unsigned)(la.nvt * la.nct)), dim3(kThreads), 0, s, la);
@@ -536,12 +534,12 @@ static hipError_t chunk_impl(const Layout& L, const T* X, const T* W, const int6
 
   {
     ProfScope ps(kPhaseLse, s);
-    hipLaunchKernelGGL(k_lse, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, part, L.nvt, zt, yc, ign, rows, lse,
-                       rowloss + c0);
+    hipLaunchKernelGGL(k_lse<T>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, part, 2 * L.nvt, Xc, W, H, V, yc,
+                       ign, rows, lse, rowloss + c0);
   }
   {
     ProfScope ps(kPhaseGrad, s);
-    hipLaunchKernelGGL(k_grad<T>, dim3((unsigned)rows), dim3(256), 0, s, z, L.ldz, V, lse, part, L.nvt, yc, ign,
+    hipLaunchKernelGGL(k_grad<T>, dim3((unsigned)rows), dim3(256), 0, s, z, L.ldz, V, lse, part, 2 * L.nvt, yc, ign,
                        nvalid);
   }
 

@@ -1,0 +1,103 @@
+"""Full-size workloads on the GPU, in the launch configuration bench.py times
+(automatic chunk size), checked against the float64 oracle.
+
+FLCE heads (Llama-3-8B, Qwen2-7B at 16K context, Gemma 256K vocabulary):
+  * against stored oracle values (tests/golden/<name>.json, written by
+    make_full_size_golden.py from the same seeded inputs, whose fingerprint is
+    checked first): the loss, 64 per-token losses, 4096 random dX entries and
+    4096 + 4 H dW entries (including the rows of the most frequent targets);
+  * against the oracle computed here, one token at a time (flce_rows_ref):
+    full dX rows and per-token losses of 6 tokens.
+Logits-only cross-entropy on the Gemma shape (fp32 logits 8192 x 256000,
+8.4 GB): per-token losses of every row and the loss from the per-row oracle,
+full dlogits rows for 16 sampled tokens.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+from gpu_helpers import TOL, ensure_built, rel_err, say, to_np
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return ensure_built()
+
+
+@pytest.mark.parametrize("name", ["llama3", "qwen2", "gemma"])
+def test_flce_full_size(name):
+    import linear_cross_entropy_05_amd as flce
+
+    with open(os.path.join(GOLDEN, f"{name}.json")) as f:
+        g = json.load(f)
+    w = si.workload(name)
+    X, W, y = si.make_inputs(w)
+    assert si.fingerprint(X, W, y) == g["fingerprint"], "seeded inputs differ from the ones the oracle saw"
+    dev = torch.device("cuda", 0)
+    say(f"[gpu] flce_fwd_bwd {name} BT={w.BT} H={w.H} V={w.V} chunk=auto")
+    loss, dX, dW, rl = flce.flce_fwd_bwd(X.to(dev), W.to(dev), y.to(dev), w.ignore_index, w.chunk_tokens,
+                                         row_loss=True)
+    torch.cuda.synchronize()
+    tl, tg = TOL[w.dtype]
+
+    el = abs(loss.item() - g["loss"]) / abs(g["loss"])
+    rows = torch.tensor(g["rows"])
+    er = rel_err(to_np(rl[rows.to(dev)]), g["row_loss"])
+    xi = torch.tensor(g["dX_idx"], device=dev)
+    wi = torch.tensor(g["dW_idx"], device=dev)
+    ex = float(np.max(np.abs(to_np(dX[xi[:, 0], xi[:, 1]]) - np.array(g["dX_val"])))) / g["max_abs_dX"]
+    ew = float(np.max(np.abs(to_np(dW[wi[:, 0], wi[:, 1]]) - np.array(g["dW_val"])))) / g["max_abs_dW"]
+    say(f"  stored: loss {loss.item():.7f} ref {g['loss']:.7f} err {el:.2e}; rows {er:.2e}; dX {ex:.2e}; dW {ew:.2e}")
+    assert el <= tl and er <= tl and ex <= tg and ew <= tg
+
+    # the oracle, here, token by token
+    pick = g["rows"][:6]
+    ref = oracle.flce_rows_ref(X, W, y, pick, g["n_valid"], w.ignore_index)
+    got = to_np(dX[torch.tensor(pick, device=dev)])
+    ex2 = float(np.max(np.abs(got - ref["dX"]))) / g["max_abs_dX"]
+    er2 = rel_err(to_np(rl[torch.tensor(pick, device=dev)]), ref["row_loss"])
+    say(f"  per-row oracle: dX rows {ex2:.2e}; token losses {er2:.2e}")
+    assert ex2 <= tg and er2 <= tl
+
+
+def test_ce_inplace_gemma_shape():
+    import linear_cross_entropy_05_amd as flce
+
+    w = si.workload("gemma")
+    X, W, y = si.make_inputs(w)
+    dev = torch.device("cuda", 0)
+    # input preparation (not the path under test): fp32 logits of the Gemma head
+    logits = X.to(dev).float() @ W.to(dev).float().T
+    del W
+    logits_cpu = logits.cpu()
+    r = np.random.default_rng(7)
+    pick = np.sort(r.choice(w.BT, 16, replace=False))
+    say(f"[gpu] ce_fwd_bwd_inplace gemma BT={w.BT} V={w.V} fp32")
+    loss, rl = flce.ce_fwd_bwd_inplace(logits, y.to(dev), w.ignore_index, row_loss=True)
+    torch.cuda.synchronize()
+    got_rows = logits[torch.tensor(pick, device=dev)].cpu()
+    got_rl = to_np(rl)
+    del logits
+    n_valid = int((y != w.ignore_index).sum())
+    ref_rl = np.zeros(w.BT)
+    for b in range(0, w.BT, 512):
+        ref_rl[b:b + 512] = oracle.ce_rows_ref(logits_cpu[b:b + 512], y[b:b + 512], n_valid,
+                                               w.ignore_index)["row_loss"]
+    ref_loss = float(ref_rl.sum() / n_valid)
+    ref_rows = oracle.ce_rows_ref(logits_cpu[pick], y[pick], n_valid, w.ignore_index)
+    el = abs(loss.item() - ref_loss) / ref_loss
+    er = rel_err(got_rl, ref_rl)
+    ed = rel_err(to_np(got_rows), ref_rows["dlogits"])
+    say(f"  loss {loss.item():.7f} ref {ref_loss:.7f} err {el:.2e}; token losses {er:.2e}; dlogits rows {ed:.2e}")
+    tl, tg = TOL["fp32"]
+    assert el <= tl and er <= tl and ed <= tg
