@@ -372,12 +372,16 @@ __device__ __forceinline__ u32x4 rsrc_words(const void* base, int64_t bytes) {
 // Written as inline asm so that the compiler does not add its own
 // conservative "wait for every outstanding load" before later LDS reads: the
 // pipeline places the waits itself (wait_vm), also in inline asm.
-__device__ __forceinline__ void dma16(u32x4 r, const char* lds, uint32_t voff, uint32_t soff) {
-  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void)lds);
+__device__ __forceinline__ void dma16(u32x4 r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(m0), "v"(voff), "s"(r), "s"(soff)
+               : "s"(lds_addr), "v"(voff), "s"(r), "s"(soff)
                : "memory", "m0");
+}
+
+// LDS byte address of a pointer into a __shared__ array, as a scalar
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void)p);
 }
 
 // K-contiguous operand, one 256-row tile.  Copy q of wave w fills rows
@@ -399,19 +403,18 @@ struct KcLoader {
       voff[q] = (uint32_t)((row * op.ld + 8 * c) * 2);
     }
   }
-  struct Stage {
-    bool tail;
-    int64_t k0;
-  };
-  __device__ __forceinline__ Stage prep(int64_t k0) const { return Stage{k0 + kBK > kend, k0}; }
-  __device__ __forceinline__ void issue_one(const Stage& st, const char* tile, int q, int wave) const {
-    const uint32_t v = (!st.tail || st.k0 + kch[q] < kend) ? voff[q] : 0x80000000u;
-    dma16(r, tile + 1024 * (wave + 4 * q), v, (uint32_t)(st.k0 * 2));
-  }
-  __device__ __forceinline__ void issue(const char* tile, int64_t k0, int wave) const {
-    const Stage st = prep(k0);
+  // tile: LDS byte address of this operand's stage tile
+  __device__ __forceinline__ void issue(uint32_t tile, int64_t k0, int wave) const {
+    const uint32_t soff = (uint32_t)(k0 * 2);
+    const uint32_t dst = tile + 1024 * wave;
+    if (k0 + kBK <= kend) {
 #pragma unroll
-    for (int q = 0; q < kLoads; ++q) issue_one(st, tile, q, wave);
+      for (int q = 0; q < kLoads; ++q) dma16(r, dst + 4096 * q, voff[q], soff);
+    } else {
+      // K tail: chunks past the bound read as zero
+#pragma unroll
+      for (int q = 0; q < kLoads; ++q) dma16(r, dst + 4096 * q, k0 + kch[q] < kend ? voff[q] : 0x80000000u, soff);
+    }
   }
   __device__ __forceinline__ u32x4 frag(const char* tile, int row, int c) const {
     return *reinterpret_cast<const u32x4*>(tile + kc_off(row, c));
@@ -438,20 +441,12 @@ struct KmLoader {
       voff[q] = (uint32_t)((k * ld + 16 * seg + 8 * (lane & 1)) * 2);
     }
   }
-  struct Stage {
-    u32x4 r;
-  };
-  __device__ __forceinline__ Stage prep(int64_t k0) const {
+  __device__ __forceinline__ void issue(uint32_t tile, int64_t k0, int wave) const {
     const int64_t nb = rows > k0 ? ((rows - k0 - 1) * ld + (cols - mn0)) * 2 : 0;
-    return Stage{rsrc_words(base + k0 * ld + mn0, nb)};
-  }
-  __device__ __forceinline__ void issue_one(const Stage& st, const char* tile, int q, int wave) const {
-    dma16(st.r, tile + 1024 * (wave + 4 * q), voff[q], 0);
-  }
-  __device__ __forceinline__ void issue(const char* tile, int64_t k0, int wave) const {
-    const Stage st = prep(k0);
+    const u32x4 r = rsrc_words(base + k0 * ld + mn0, nb);
+    const uint32_t dst = tile + 1024 * wave;
 #pragma unroll
-    for (int q = 0; q < kLoads; ++q) issue_one(st, tile, q, wave);
+    for (int q = 0; q < kLoads; ++q) dma16(r, dst + 4096 * q, voff[q], 0);
   }
   // fragment of MN columns nb .. nb + 31, K rows 16 s + 8 (lane / 32) .. + 7
   __device__ __forceinline__ u32x4 frag(const char* tile, int nb, int s, int lane) const {
@@ -500,7 +495,7 @@ template <bool kAKMajor, bool kBKMajor, int NS>
 __device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, int64_t m0, const Operand<__bf16>& B,
                                          int64_t n0, int64_t k0, int64_t k1, f32x16 (&acc)[4][4]) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wy = wave >> 1, wx = wave & 1;
   const int nk = (int)((k1 - k0 + kBK - 1) / kBK);
 #pragma unroll
@@ -513,11 +508,12 @@ __device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, i
   LoaderT<kBKMajor> lb;
   la.init(A, m0, wave, lane);
   lb.init(B, n0, wave, lane);
+  const uint32_t lds0 = lds_addr(smem);
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
     if (st < nk) {
-      la.issue(smem + st * kStage, k0 + (int64_t)st * kBK, wave);
-      lb.issue(smem + st * kStage + kOp, k0 + (int64_t)st * kBK, wave);
+      la.issue(lds0 + st * kStage, k0 + (int64_t)st * kBK, wave);
+      lb.issue(lds0 + st * kStage + kOp, k0 + (int64_t)st * kBK, wave);
     }
   wait_stages(nk - 1 < NS - 2 ? nk - 1 : NS - 2);
   __syncthreads();
@@ -528,8 +524,42 @@ __device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, i
 #pragma unroll
   for (int j = 0; j < 4; ++j) fb[0][j] = read_frag<kBKMajor>(lb, smem + kOp, wx * 128 + 32 * j, 0, lane);
 
-  for (int kt = 0; kt < nk; ++kt) {
+  // every iteration of this loop has a next stage; the last stage follows
+  for (int kt = 0; kt + 1 < nk; ++kt) {
     const char* cur = smem + (kt % NS) * kStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[1][i] = read_frag<kAKMajor>(la, cur, wy * 128 + 32 * i, 1, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[1][j] = read_frag<kBKMajor>(lb, cur + kOp, wx * 128 + 32 * j, 1, lane);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mma_chunk<__bf16>(fa[0][i], fb[0][j], acc[i][j]);
+    // stage kt + 1 landed (this wave's copies), then everyone's; buffer
+    // (kt - 1) % NS is no longer read by anyone
+    const int ahead = nk - 2 - kt;
+    wait_stages(ahead < NS - 3 ? ahead : NS - 3);
+    __syncthreads();
+    if (kt + NS - 1 < nk) {
+      const uint32_t dst = lds0 + ((kt + NS - 1) % NS) * kStage;
+      la.issue(dst, k0 + (int64_t)(kt + NS - 1) * kBK, wave);
+      lb.issue(dst + kOp, k0 + (int64_t)(kt + NS - 1) * kBK, wave);
+    }
+    const char* nxt = smem + ((kt + 1) % NS) * kStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[0][i] = read_frag<kAKMajor>(la, nxt, wy * 128 + 32 * i, 0, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[0][j] = read_frag<kBKMajor>(lb, nxt + kOp, wx * 128 + 32 * j, 0, lane);
+    // keep these reads ahead of the MFMAs below (they feed the next step)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mma_chunk<__bf16>(fa[1][i], fb[1][j], acc[i][j]);
+  }
+  {
+    const char* cur = smem + ((nk - 1) % NS) * kStage;
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[1][i] = read_frag<kAKMajor>(la, cur, wy * 128 + 32 * i, 1, lane);
 #pragma unroll
@@ -538,23 +568,6 @@ __device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, i
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mma_chunk<__bf16>(fa[0][i], fb[0][j], acc[i][j]);
-    if (kt + 1 < nk) {
-      // stage kt + 1 landed (this wave's copies), then everyone's; buffer
-      // (kt - 1) % NS is no longer read by anyone
-      const int ahead = nk - 2 - kt;
-      wait_stages(ahead < NS - 3 ? ahead : NS - 3);
-      __syncthreads();
-      if (kt + NS - 1 < nk) {
-        char* dst = smem + ((kt + NS - 1) % NS) * kStage;
-        la.issue(dst, k0 + (int64_t)(kt + NS - 1) * kBK, wave);
-        lb.issue(dst + kOp, k0 + (int64_t)(kt + NS - 1) * kBK, wave);
-      }
-      const char* nxt = smem + ((kt + 1) % NS) * kStage;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fa[0][i] = read_frag<kAKMajor>(la, nxt, wy * 128 + 32 * i, 0, lane);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) fb[0][j] = read_frag<kBKMajor>(lb, nxt + kOp, wx * 128 + 32 * j, 0, lane);
-    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
