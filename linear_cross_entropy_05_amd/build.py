@@ -62,19 +62,19 @@ def _compile(src: str, verbose: bool, extra: list[str]) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+def build(verbose: bool = False, extra: list[str] | None = None, out: str = LIB) -> str:
     """Compile every HIP source for gfx950 and link libflce.so; return its path."""
     os.makedirs(BUILD, exist_ok=True)
     extra = extra or []
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose, extra), SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def main(argv=None) -> int:

@@ -541,12 +541,12 @@ __device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, i
     const int ahead = nk - 2 - kt;
     wait_stages(ahead < NS - 3 ? ahead : NS - 3);
     __syncthreads();
+    const char* nxt = smem + ((kt + 1) % NS) * kStage;
     if (kt + NS - 1 < nk) {
       const uint32_t dst = lds0 + ((kt + NS - 1) % NS) * kStage;
       la.issue(dst, k0 + (int64_t)(kt + NS - 1) * kBK, wave);
       lb.issue(dst + kOp, k0 + (int64_t)(kt + NS - 1) * kBK, wave);
     }
-    const char* nxt = smem + ((kt + 1) % NS) * kStage;
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[0][i] = read_frag<kAKMajor>(la, nxt, wy * 128 + 32 * i, 0, lane);
 #pragma unroll
@@ -580,7 +580,18 @@ __device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, i
 
 // acc = A[m0:m0+256, k0:k1) * B[n0:n0+256, k0:k1)^T: the direct-to-LDS
 // pipeline for bf16, the register-staged loop for fp32.
-constexpr int kPipeStages = 4;
+#ifndef FLCE_PIPE_STAGES
+#define FLCE_PIPE_STAGES 4
+#endif
+constexpr int kPipeStages = FLCE_PIPE_STAGES;
+static_assert(kPipeStages * pipe::kStage <= 160 * 1024, "LDS");
+constexpr int kGemmLdsBytes = kPipeStages * pipe::kStage > kLdsBytes ? kPipeStages * pipe::kStage : kLdsBytes;
+
+// Tile-order group size (consecutive tile rows walked column by column).
+#ifndef FLCE_TILE_GROUP
+#define FLCE_TILE_GROUP 4
+#endif
+constexpr int kTileGroup = FLCE_TILE_GROUP;
 
 template <typename T, bool kAKMajor, bool kBKMajor>
 __device__ __forceinline__ void gemm_mainloop(char* smem, const Operand<T>& A, int64_t m0, const Operand<T>& B,

@@ -120,9 +120,9 @@ __device__ __forceinline__ void store4_ptr(float* p, float a, float b, float c, 
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  __shared__ __attribute__((aligned(16))) char smem[kGemmLdsBytes];
   int64_t vt, ct;
-  grouped_tile(xcd_tile(blockIdx.x, a.nvt * a.nct), a.nvt, a.nct, 4, vt, ct);
+  grouped_tile(xcd_tile(blockIdx.x, a.nvt * a.nct), a.nvt, a.nct, kTileGroup, vt, ct);
   const int64_t v0 = vt * kTile, c0 = ct * kTile;
 
   f32x16 acc[4][4];
@@ -294,7 +294,7 @@ struct DxArgs {
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_dx(DxArgs<T> a) {
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  __shared__ __attribute__((aligned(16))) char smem[kGemmLdsBytes];
   const int64_t tile = blockIdx.x;
   const int64_t mt = tile / a.nnt, nt = tile % a.nnt;
   const int64_t m0 = mt * kTile, n0 = nt * kTile;
@@ -364,9 +364,9 @@ struct DwArgs {
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  __shared__ __attribute__((aligned(16))) char smem[kGemmLdsBytes];
   int64_t vt, ht;
-  grouped_tile(xcd_tile(blockIdx.x, a.nvt * a.nht), a.nvt, a.nht, 4, vt, ht);
+  grouped_tile(xcd_tile(blockIdx.x, a.nvt * a.nht), a.nvt, a.nht, kTileGroup, vt, ht);
   const int64_t v0 = vt * kTile, h0 = ht * kTile;
 
   // X_chunk^T as the A operand (rows h) and G^T as B (columns v): each lane
