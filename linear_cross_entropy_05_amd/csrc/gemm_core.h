@@ -323,35 +323,40 @@ __device__ __forceinline__ void mainloop_regstage(char* smem, const Operand<T>& 
 // ---- bf16 pipelined main loop -------------------------------------------------
 //
 // Global -> LDS copies go straight into LDS (buffer_load ... lds, 16 bytes per
-// lane; a wave's instruction fills 1 KiB of LDS in lane order), NS stages of
-// 32 bf16 of K deep, so loads for stage k + NS - 1 are in flight while stage k
-// is multiplied.  Tiles in LDS:
-//   K-contiguous operand: 256 rows x 64 bytes; 16-byte chunk c of row r at
-//     slot c ^ ((r >> 1) ^ (r >> 3)) & 3 (the copying lane picks the chunk
-//     that belongs at its slot).  Fragments: ds_read_b128.
-//   K-major operand: 32 K rows x 512 bytes (256 MN values); 32-byte segment
+// lane; a wave's instruction fills 1 KiB of LDS in lane order).  A stage is
+// 64 bf16 of K, so every tile row of a K-contiguous operand is one whole
+// 128-byte segment per stage: the L2 serves it as one 128-byte request (32 of
+// K would be a 64-byte request, and the request rate, not bytes, is what
+// limits these copies).  Two stages of 64 KiB: the copy of stage k + 2 starts
+// as soon as everyone is done reading stage k and lands while stage k + 1 is
+// multiplied.  Tiles in LDS:
+//   K-contiguous operand: 256 rows x 128 bytes; 16-byte chunk c of row r at
+//     slot c ^ ((r' >> 1) ^ (r' >> 4)) & 7, r' = r % 32 (the copying lane picks
+//     the chunk that belongs at its slot).  Fragments: ds_read_b128.
+//   K-major operand: 64 K rows x 512 bytes (256 MN values); 32-byte segment
 //     s of K row k at position s ^ {0, 2, 5, 7}[k % 4].  Fragments: two
 //     ds_read_b64_tr_b16, which hand lane i of each 16-lane group element t
 //     of the 8 bytes read by lane 4 t + i / 4 of that group (so lane 4 t + q
 //     points at K row t, MN columns 4 q .. 4 q + 3, and lane i receives MN
 //     column i for four consecutive K rows).
-// Both swizzles keep fragment reads free of LDS bank conflicts.
-// Each stage has one barrier, placed between its two 16-MFMA steps so the
-// MFMAs already issued cover the wait and the next stage's first fragment
-// reads overlap the second step.
+// Both swizzles keep fragment reads free of LDS bank conflicts (measured with
+// the SQ_LDS_BANK_CONFLICT counter).
+// Each stage is four 16-MFMA steps; the fragments of step s + 1 are read
+// while step s multiplies.  One barrier per stage, before its last step.
 namespace pipe {
 
-constexpr int kBK = 32;           // bf16 K per stage
-constexpr int kRowB = 64;         // bytes per K-contiguous tile row per stage
-constexpr int kOp = 256 * kRowB;  // 16 KiB per operand per stage
-constexpr int kStage = 2 * kOp;   // 32 KiB
-constexpr int kLoads = 4;         // 1 KiB copies per wave per operand per stage
+constexpr int kBK = 64;           // bf16 K per stage
+constexpr int kRowB = 128;        // bytes per K-contiguous tile row per stage
+constexpr int kOp = 256 * kRowB;  // 32 KiB per operand per stage
+constexpr int kStage = 2 * kOp;   // 64 KiB
+constexpr int kLoads = 8;         // 1 KiB copies per wave per operand per stage
 
 typedef __attribute__((address_space(3))) void* lds_void;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
+__device__ __forceinline__ uint32_t kc_sw(uint32_t r) { return ((r >> 1) ^ (r >> 4)) & 7u; }
 __device__ __forceinline__ uint32_t kc_off(uint32_t r, uint32_t c) {
-  return r * kRowB + (((c ^ (r >> 1) ^ (r >> 3)) & 3u) << 4);
+  return r * kRowB + (((c ^ kc_sw(r & 31u)) & 7u) << 4);
 }
 __device__ __forceinline__ uint32_t km_sw(uint32_t k) { return (0x7520u >> (4 * (k & 3u))) & 15u; }
 __device__ __forceinline__ uint32_t km_off(uint32_t k, uint32_t n) {
@@ -371,7 +376,9 @@ __device__ __forceinline__ u32x4 rsrc_words(const void* base, int64_t bytes) {
 // 16 bytes per lane from the buffer straight into LDS at lds + 16 * lane.
 // Written as inline asm so that the compiler does not add its own
 // conservative "wait for every outstanding load" before later LDS reads: the
-// pipeline places the waits itself (wait_vm), also in inline asm.
+// pipeline places the waits itself (wait_vm), also in inline asm.  The
+// bounds check of a raw buffer covers the VGPR offset, so every offset that
+// can leave the operand lives there; the scalar offset only carries k0.
 __device__ __forceinline__ void dma16(u32x4 r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
@@ -385,23 +392,21 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 }
 
 // K-contiguous operand, one 256-row tile.  Copy q of wave w fills rows
-// 16 g .. 16 g + 15 (g = w + 4 q); lane i fills row 16 g + i / 4, slot i % 4.
+// 8 w + 32 q .. + 7; lane i fills row 8 w + 32 q + i / 8, slot i % 8.
 struct KcLoader {
   u32x4 r;
   uint32_t voff[kLoads];
-  uint32_t kch[kLoads];  // K offset (elements) of the chunk each copy reads
+  uint32_t kch;  // K offset (elements) of this lane's chunk, the same for every copy
   int64_t kend;
   __device__ __forceinline__ void init(const Operand<__bf16>& op, int64_t mn0, int wave, int lane) {
     const int64_t nrows = op.rows - mn0 < kTile ? op.rows - mn0 : kTile;
     r = rsrc_words(op.base + mn0 * op.ld, nrows * op.ld * 2);
     kend = op.cols;
+    const uint32_t row = 8 * wave + (lane >> 3);  // < 32: the swizzle is that of every copy's row
+    const uint32_t c = ((lane & 7) ^ kc_sw(row)) & 7u;
+    kch = 8 * c;
 #pragma unroll
-    for (int q = 0; q < kLoads; ++q) {
-      const uint32_t row = 16 * (wave + 4 * q) + (lane >> 2);
-      const uint32_t c = ((lane & 3) ^ (row >> 1) ^ (row >> 3)) & 3u;
-      kch[q] = 8 * c;
-      voff[q] = (uint32_t)((row * op.ld + 8 * c) * 2);
-    }
+    for (int q = 0; q < kLoads; ++q) voff[q] = (uint32_t)(((row + 32 * q) * op.ld + 8 * c) * 2);
   }
   // tile: LDS byte address of this operand's stage tile
   __device__ __forceinline__ void issue(uint32_t tile, int64_t k0, int wave) const {
@@ -412,8 +417,9 @@ struct KcLoader {
       for (int q = 0; q < kLoads; ++q) dma16(r, dst + 4096 * q, voff[q], soff);
     } else {
       // K tail: chunks past the bound read as zero
+      const bool in = k0 + kch < kend;
 #pragma unroll
-      for (int q = 0; q < kLoads; ++q) dma16(r, dst + 4096 * q, k0 + kch[q] < kend ? voff[q] : 0x80000000u, soff);
+      for (int q = 0; q < kLoads; ++q) dma16(r, dst + 4096 * q, in ? voff[q] : 0x80000000u, soff);
     }
   }
   __device__ __forceinline__ u32x4 frag(const char* tile, int row, int c) const {
@@ -421,9 +427,9 @@ struct KcLoader {
   }
 };
 
-// K-major operand (memory rows are K): copy q of wave w fills K rows 2 g and
-// 2 g + 1 (g = w + 4 q); lane i fills K row 2 g + i / 32, 16 bytes at
-// position (i % 32) / 2, half i % 2.
+// K-major operand (memory rows are K): copy q of wave w fills K rows
+// 2 w + 8 q and 2 w + 8 q + 1; lane i fills K row 2 w + 8 q + i / 32, 16
+// bytes at position (i % 32) / 2, half i % 2.
 struct KmLoader {
   const __bf16* base;
   int64_t ld, rows, cols, mn0;
@@ -434,14 +440,15 @@ struct KmLoader {
     rows = op.rows;
     cols = op.cols;
     mn0 = mn0_;
+    const uint32_t k = 2 * wave + (lane >> 5);  // k % 4, hence the swizzle, is that of every copy
+    const uint32_t seg = (((lane & 31) >> 1) ^ km_sw(k)) & 15u;
 #pragma unroll
-    for (int q = 0; q < kLoads; ++q) {
-      const uint32_t k = 2 * (wave + 4 * q) + (lane >> 5);
-      const uint32_t seg = (((lane & 31) >> 1) ^ km_sw(k)) & 15u;
-      voff[q] = (uint32_t)((k * ld + 16 * seg + 8 * (lane & 1)) * 2);
-    }
+    for (int q = 0; q < kLoads; ++q) voff[q] = (uint32_t)(((k + 8 * q) * ld + 16 * seg + 8 * (lane & 1)) * 2);
   }
   __device__ __forceinline__ void issue(uint32_t tile, int64_t k0, int wave) const {
+    // the buffer ends at the last element of the operand: K rows past it and
+    // MN columns past it on the last K row read as zero (MN columns past the
+    // tile edge on earlier rows feed only outputs that are never stored)
     const int64_t nb = rows > k0 ? ((rows - k0 - 1) * ld + (cols - mn0)) * 2 : 0;
     const u32x4 r = rsrc_words(base + k0 * ld + mn0, nb);
     const uint32_t dst = tile + 1024 * wave;
@@ -478,20 +485,25 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// wait until at most n (0..3) stages of this wave's copies are in flight
-__device__ __forceinline__ void wait_stages(int n) {
-  constexpr int L = 2 * kLoads;
-  if (n <= 0)
-    wait_vm<0>();
-  else if (n == 1)
-    wait_vm<L>();
-  else if (n == 2)
-    wait_vm<2 * L>();
-  else
-    wait_vm<3 * L>();
+// fragments of step s (16 of K) of a stage: this wave's four A row blocks and
+// four B row blocks
+template <bool kAKMajor, bool kBKMajor>
+__device__ __forceinline__ void load_step(const LoaderT<kAKMajor>& la, const LoaderT<kBKMajor>& lb, const char* tile,
+                                          int s, int wy, int wx, int lane, u32x4 (&fa)[4], u32x4 (&fb)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[i] = read_frag<kAKMajor>(la, tile, wy * 128 + 32 * i, s, lane);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fb[j] = read_frag<kBKMajor>(lb, tile + kOp, wx * 128 + 32 * j, s, lane);
 }
 
-template <bool kAKMajor, bool kBKMajor, int NS>
+__device__ __forceinline__ void mma_step(const u32x4 (&fa)[4], const u32x4 (&fb)[4], f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = mma_chunk<__bf16>(fa[i], fb[j], acc[i][j]);
+}
+
+template <bool kAKMajor, bool kBKMajor>
 __device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, int64_t m0, const Operand<__bf16>& B,
                                          int64_t n0, int64_t k0, int64_t k1, f32x16 (&acc)[4][4]) {
   const int tid = threadIdx.x;
@@ -509,69 +521,51 @@ __device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, i
   la.init(A, m0, wave, lane);
   lb.init(B, n0, wave, lane);
   const uint32_t lds0 = lds_addr(smem);
-#pragma unroll
-  for (int st = 0; st < NS - 1; ++st)
-    if (st < nk) {
-      la.issue(lds0 + st * kStage, k0 + (int64_t)st * kBK, wave);
-      lb.issue(lds0 + st * kStage + kOp, k0 + (int64_t)st * kBK, wave);
-    }
-  wait_stages(nk - 1 < NS - 2 ? nk - 1 : NS - 2);
+  la.issue(lds0, k0, wave);
+  lb.issue(lds0 + kOp, k0, wave);
+  if (nk > 1) {
+    la.issue(lds0 + kStage, k0 + kBK, wave);
+    lb.issue(lds0 + kStage + kOp, k0 + kBK, wave);
+    wait_vm<2 * kLoads>();
+  } else {
+    wait_vm<0>();
+  }
   __syncthreads();
 
   u32x4 fa[2][4], fb[2][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) fa[0][i] = read_frag<kAKMajor>(la, smem, wy * 128 + 32 * i, 0, lane);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) fb[0][j] = read_frag<kBKMajor>(lb, smem + kOp, wx * 128 + 32 * j, 0, lane);
-
+  load_step<kAKMajor, kBKMajor>(la, lb, smem, 0, wy, wx, lane, fa[0], fb[0]);
   // every iteration of this loop has a next stage; the last stage follows
   for (int kt = 0; kt + 1 < nk; ++kt) {
-    const char* cur = smem + (kt % NS) * kStage;
+    const char* cur = smem + (kt & 1) * kStage;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[1][i] = read_frag<kAKMajor>(la, cur, wy * 128 + 32 * i, 1, lane);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fb[1][j] = read_frag<kBKMajor>(lb, cur + kOp, wx * 128 + 32 * j, 1, lane);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mma_chunk<__bf16>(fa[0][i], fb[0][j], acc[i][j]);
-    // stage kt + 1 landed (this wave's copies), then everyone's; buffer
-    // (kt - 1) % NS is no longer read by anyone
-    const int ahead = nk - 2 - kt;
-    wait_stages(ahead < NS - 3 ? ahead : NS - 3);
-    __syncthreads();
-    const char* nxt = smem + ((kt + 1) % NS) * kStage;
-    if (kt + NS - 1 < nk) {
-      const uint32_t dst = lds0 + ((kt + NS - 1) % NS) * kStage;
-      la.issue(dst, k0 + (int64_t)(kt + NS - 1) * kBK, wave);
-      lb.issue(dst + kOp, k0 + (int64_t)(kt + NS - 1) * kBK, wave);
+    for (int s = 0; s < 3; ++s) {
+      load_step<kAKMajor, kBKMajor>(la, lb, cur, s + 1, wy, wx, lane, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+      // keep these reads ahead of the MFMAs below
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step(fa[s & 1], fb[s & 1], acc);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[0][i] = read_frag<kAKMajor>(la, nxt, wy * 128 + 32 * i, 0, lane);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fb[0][j] = read_frag<kBKMajor>(lb, nxt + kOp, wx * 128 + 32 * j, 0, lane);
-    // keep these reads ahead of the MFMAs below (they feed the next step)
+    // stage kt + 1 landed (this wave's copies), then everyone's; nobody
+    // reads stage kt any more
+    wait_vm<0>();
+    __syncthreads();
+    if (kt + 2 < nk) {
+      const uint32_t dst = lds0 + (kt & 1) * kStage;
+      la.issue(dst, k0 + (int64_t)(kt + 2) * kBK, wave);
+      lb.issue(dst + kOp, k0 + (int64_t)(kt + 2) * kBK, wave);
+    }
+    load_step<kAKMajor, kBKMajor>(la, lb, smem + ((kt + 1) & 1) * kStage, 0, wy, wx, lane, fa[0], fb[0]);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mma_chunk<__bf16>(fa[1][i], fb[1][j], acc[i][j]);
+    mma_step(fa[1], fb[1], acc);
   }
   {
-    const char* cur = smem + ((nk - 1) % NS) * kStage;
+    const char* cur = smem + ((nk - 1) & 1) * kStage;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[1][i] = read_frag<kAKMajor>(la, cur, wy * 128 + 32 * i, 1, lane);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) fb[1][j] = read_frag<kBKMajor>(lb, cur + kOp, wx * 128 + 32 * j, 1, lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mma_chunk<__bf16>(fa[0][i], fb[0][j], acc[i][j]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mma_chunk<__bf16>(fa[1][i], fb[1][j], acc[i][j]);
+    for (int s = 0; s < 3; ++s) {
+      load_step<kAKMajor, kBKMajor>(la, lb, cur, s + 1, wy, wx, lane, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step(fa[s & 1], fb[s & 1], acc);
+    }
+    mma_step(fa[1], fb[1], acc);
   }
   __syncthreads();  // LDS free for the epilogue
 }
@@ -580,16 +574,12 @@ __device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, i
 
 // acc = A[m0:m0+256, k0:k1) * B[n0:n0+256, k0:k1)^T: the direct-to-LDS
 // pipeline for bf16, the register-staged loop for fp32.
-#ifndef FLCE_PIPE_STAGES
-#define FLCE_PIPE_STAGES 4
-#endif
-constexpr int kPipeStages = FLCE_PIPE_STAGES;
-static_assert(kPipeStages * pipe::kStage <= 160 * 1024, "LDS");
-constexpr int kGemmLdsBytes = kPipeStages * pipe::kStage > kLdsBytes ? kPipeStages * pipe::kStage : kLdsBytes;
+static_assert(2 * pipe::kStage <= kLdsBytes, "LDS");
+constexpr int kGemmLdsBytes = kLdsBytes;
 
 // Tile-order group size (consecutive tile rows walked column by column).
 #ifndef FLCE_TILE_GROUP
-#define FLCE_TILE_GROUP 4
+#define FLCE_TILE_GROUP 8
 #endif
 constexpr int kTileGroup = FLCE_TILE_GROUP;
 
@@ -597,7 +587,7 @@ template <typename T, bool kAKMajor, bool kBKMajor>
 __device__ __forceinline__ void gemm_mainloop(char* smem, const Operand<T>& A, int64_t m0, const Operand<T>& B,
                                               int64_t n0, int64_t k0, int64_t k1, f32x16 (&acc)[4][4]) {
   if constexpr (sizeof(T) == 2)
-    pipe::mainloop<kAKMajor, kBKMajor, kPipeStages>(smem, A, m0, B, n0, k0, k1, acc);
+    pipe::mainloop<kAKMajor, kBKMajor>(smem, A, m0, B, n0, k0, k1, acc);
   else
     mainloop_regstage<T, kAKMajor, kBKMajor>(smem, A, m0, B, n0, k0, k1, acc);
 }

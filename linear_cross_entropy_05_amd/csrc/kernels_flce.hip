@@ -118,6 +118,13 @@ __device__ __forceinline__ void store4_ptr(float* p, float a, float b, float c, 
   *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
 }
 
+// LDS row pitch (bytes) of the staged bf16 chunk block in the logits epilogue
+constexpr int kZPitch = 264;
+// cache-policy bits of a buffer store that streams past the L2 (nt): the chunk
+// buffer and dW are far larger than the L2, and keeping them out leaves it
+// to the GEMM operands
+constexpr int kNonTemporal = 2;
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char smem[kGemmLdsBytes];
@@ -166,14 +173,43 @@ __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
     // most of the softmax mass are then small numbers and keep their
     // precision.  Rows are padded to a multiple of 256, so a tile never
     // crosses into the next row; entries past V fill the padding.
+    if constexpr (sizeof(T) == 2) {
+      // A lane holds 16-byte pieces of one token row, so direct stores would
+      // scatter 32 rows per instruction.  Stage the wave's 32 x 128 block in
+      // LDS (rows 264 bytes apart: both passes below are free of bank
+      // conflicts) and store two whole 256-byte row segments per instruction.
+      char* st = smem + wave * (32 * kZPitch);
+      const int t = lane & 31, hh = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x16& q = acc[i][j];
-        store4(zr, lane_off + j * row32 + (uint32_t)((32 * i + 8 * g) * (int64_t)sizeof(T)), q[4 * g] - m,
-               q[4 * g + 1] - m, q[4 * g + 2] - m, q[4 * g + 3] - m, (T*)nullptr);
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& q = acc[i][j];
+          const bf16x2 lo = __builtin_convertvector((f32x2){q[4 * g] - m, q[4 * g + 1] - m}, bf16x2);
+          const bf16x2 hi = __builtin_convertvector((f32x2){q[4 * g + 2] - m, q[4 * g + 3] - m}, bf16x2);
+          *reinterpret_cast<uint2*>(st + t * kZPitch + 2 * (32 * i + 8 * g + 4 * hh)) =
+              uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        }
+      const uint32_t seg_off = (uint32_t)((v0 + wy * 128 + 4 * t) * 2);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int r = 2 * k + hh;
+        const uint2 d = *reinterpret_cast<const uint2*>(st + r * kZPitch + 8 * t);
+        typedef int i32x2 __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)d.x, (int)d.y}, zr,
+                                              (int)((uint32_t)(wx * 128 + 32 * j + r) * (uint32_t)(a.ldz * 2) + seg_off),
+                                              0, kNonTemporal);
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& q = acc[i][j];
+          store4(zr, lane_off + j * row32 + (uint32_t)((32 * i + 8 * g) * (int64_t)sizeof(T)), q[4 * g] - m,
+                 q[4 * g + 1] - m, q[4 * g + 2] - m, q[4 * g + 3] - m, (T*)nullptr);
+        }
+    }
   }
 }
 
@@ -370,34 +406,53 @@ __global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
   const int64_t v0 = vt * kTile, h0 = ht * kTile;
 
   // X_chunk^T as the A operand (rows h) and G^T as B (columns v): each lane
-  // then holds four consecutive h of one dW row, one 16-byte access each
+  // then holds four consecutive h of one dW row
   f32x16 acc[4][4];
   gemm_mainloop<T, true, true>(smem, a.X, h0, a.G, v0, 0, a.rows, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // accumulator (i, j, e): h = h0 + hw + 32 i + 8 (e / 4) + e % 4, v = v0 + vw + 32 j
-  const int hw = (wave >> 1) * 128 + 4 * (lane >> 5);
-  const int vw = (wave & 1) * 128 + (lane & 31);
+  // accumulator (i, j, e): h = h0 + (wave / 2) 128 + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4,
+  //                        v = v0 + (wave % 2) 128 + 32 j + lane % 32
   const int vlim = (int)(a.V - v0 < kTile ? a.V - v0 : kTile);
   const int hlim = (int)(a.H - h0 < kTile ? a.H - h0 : kTile);
   float* base = a.dw + v0 * a.H + h0;
   const uint32_t H = (uint32_t)a.H;
-  const bool full = vlim == kTile && hlim == kTile;
+  // A lane holds 16-byte pieces of one dW row (v), so direct accesses would
+  // touch 32 rows per instruction.  Per 32-row block, stage the wave's
+  // 32 x 128 floats in LDS (16-byte chunk c of row r at chunk c ^ r: both
+  // passes free of bank conflicts) and read/write two whole 512-byte row
+  // segments per instruction.
+  char* st = smem + wave * (32 * 512);
+  const int t = lane & 31, hh = lane >> 5;
+  const int hcol = (wave >> 1) * 128 + 4 * t;  // this lane's 4 columns in the staged pass
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int v = vw + 32 * j;
-    if (!full && v >= vlim) continue;
+    const int vrow = (wave & 1) * 128 + 32 * j;  // first row of this block
+    f32x4 old[16];
+    if (!a.first) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int v = vrow + 2 * k + hh;
+        old[k] = (v < vlim && hcol < hlim) ? *reinterpret_cast<const f32x4*>(base + ((uint32_t)v * H + (uint32_t)hcol))
+                                           : f32x4{};
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int h = hw + 32 * i + 8 * g;
-        if (full || h < hlim) {
-          f32x4* p = reinterpret_cast<f32x4*>(base + ((uint32_t)v * H + (uint32_t)h));
-          const f32x4 r = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-          *p = a.first ? r : *p + r;
-        }
+        const int c = 8 * i + 2 * g + hh;
+        *reinterpret_cast<f32x4*>(st + t * 512 + ((c ^ t) << 4)) =
+            f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
       }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int r = 2 * k + hh, v = vrow + r;
+      f32x4 d = *reinterpret_cast<const f32x4*>(st + r * 512 + ((t ^ r) << 4));
+      if (!a.first) d += old[k];
+      if (v < vlim && hcol < hlim)
+        __builtin_nontemporal_store(d, reinterpret_cast<f32x4*>(base + ((uint32_t)v * H + (uint32_t)hcol)));
+    }
   }
 }
 
