@@ -323,7 +323,7 @@ template <typename T>
 struct DxArgs {
   Operand<T> G;  // chunk buffer [rows, ldz], K = V contiguous: the GEMM's B (columns c)
   Operand<T> W;  // [V, H] read K-major: the GEMM's A (rows h)
-  int64_t V, H, rows, nmt, nnt, ksplit;
+  int64_t V, H, rows, nmt, nnt, ksplit, splits;
   T* dx;         // [rows, H] when not split
   float* part;   // [splits, rows, H] when split
 };
@@ -331,10 +331,16 @@ struct DxArgs {
 template <typename T>
 __global__ __launch_bounds__(256) void k_dx(DxArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char smem[kGemmLdsBytes];
-  const int64_t tile = blockIdx.x;
-  const int64_t mt = tile / a.nnt, nt = tile % a.nnt;
+  // one 1-D grid over (split, tile): each XCD walks a contiguous range, so
+  // its concurrently running tiles are neighbours of one split and share
+  // operand blocks in its L2
+  const int64_t ntiles = a.nmt * a.nnt;
+  const int64_t t = xcd_tile(blockIdx.x, ntiles * a.splits);
+  const int64_t split = t / ntiles;
+  int64_t mt, nt;
+  grouped_tile(t - split * ntiles, a.nmt, a.nnt, 4, mt, nt);
   const int64_t m0 = mt * kTile, n0 = nt * kTile;
-  const int64_t k0 = (int64_t)blockIdx.y * a.ksplit;
+  const int64_t k0 = split * a.ksplit;
   const int64_t k1 = k0 + a.ksplit < a.V ? k0 + a.ksplit : a.V;
   Operand<T> G = a.G, W = a.W;
   if (k1 < G.cols) G.cols = k1;
@@ -351,8 +357,8 @@ __global__ __launch_bounds__(256) void k_dx(DxArgs<T> a) {
   const int cw = (wave & 1) * 128 + (lane & 31);
   const int mlim = (int)(a.rows - m0 < kTile ? a.rows - m0 : kTile);
   const int nlim = (int)(a.H - n0 < kTile ? a.H - n0 : kTile);
-  const bool split = gridDim.y > 1;
-  float* pbase = a.part + (int64_t)blockIdx.y * a.rows * a.H + m0 * a.H + n0;
+  const bool split_k = a.splits > 1;
+  float* pbase = a.part + split * a.rows * a.H + m0 * a.H + n0;
   T* dbase = a.dx + m0 * a.H + n0;
   const uint32_t H = (uint32_t)a.H;
   const bool full = mlim == kTile && nlim == kTile;
@@ -368,7 +374,7 @@ __global__ __launch_bounds__(256) void k_dx(DxArgs<T> a) {
         if (full || h < nlim) {
           const uint32_t off = (uint32_t)c * H + (uint32_t)h;
           const f32x16& q = acc[i][j];
-          if (split)
+          if (split_k)
             *reinterpret_cast<f32x4*>(pbase + off) = f32x4{q[4 * g], q[4 * g + 1], q[4 * g + 2], q[4 * g + 3]};
           else
             store4_ptr(dbase + off, q[4 * g], q[4 * g + 1], q[4 * g + 2], q[4 * g + 3]);
@@ -610,11 +616,12 @@ static hipError_t chunk_impl(const Layout& L, const T* X, const T* W, const int6
   const int64_t ks = kStageK<T>;
   da.ksplit = ((V + L.splits - 1) / L.splits + ks - 1) / ks * ks;
   const int64_t splits = (V + da.ksplit - 1) / da.ksplit;
+  da.splits = splits;
   da.dx = dX + c0 * H;
   da.part = reinterpret_cast<float*>(ws + L.off_dxpart);
   {
     ProfScope ps(kPhaseDx, s);
-    hipLaunchKernelGGL(k_dx<T>, dim3((unsigned)(da.nmt * da.nnt), (unsigned)splits), dim3(kThreads), 0, s, da);
+    hipLaunchKernelGGL(k_dx<T>, dim3((unsigned)(da.nmt * da.nnt * splits)), dim3(kThreads), 0, s, da);
   }
   if (splits > 1) {
     const int64_t n = rows * H;
