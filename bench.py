@@ -34,7 +34,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def gpu_bench(w, steps, warmup):
+def gpu_bench(w, steps, warmup, forward=True):
     import torch
 
     import linear_cross_entropy_05_amd as flce
@@ -86,6 +86,11 @@ def gpu_bench(w, steps, warmup):
         wall1 = time.perf_counter()
     ms = t0.elapsed_time(t1) / steps
     wall_ms = (wall1 - wall0) * 1e3 / steps
+
+    # forward only (evaluation path), timed separately and reported as context
+    fwd_ms = None
+    if forward:
+        fwd_ms = time_forward(flce, w, Xd, Wd, yd, steps, stream, float(out[0].item()))
     err = int(out[3].item())
     if err != 0:
         raise RuntimeError(f"device reported error flag {err}")
@@ -95,8 +100,35 @@ def gpu_bench(w, steps, warmup):
                for k in kt.ms if kt.launches[k]}
     log(f"[bench] {ms:.3f} ms/step (wall {wall_ms:.3f}); kernels: "
         + ", ".join(f"{k} {v['ms_per_step']:.3f}" for k, v in kernels.items()))
-    return {"ms": ms, "C": C, "ws_bytes": ws_bytes, "peak_extra": peak_extra, "loss": loss, "kernels": kernels,
+    return {"ms": ms, "fwd_ms": fwd_ms, "C": C, "ws_bytes": ws_bytes, "peak_extra": peak_extra, "loss": loss,
+            "kernels": kernels,
             "cus": props.multi_processor_count, "arch": getattr(props, "gcnArchName", "?")}
+
+
+def time_forward(flce, w, Xd, Wd, yd, steps, stream, loss_fwd_bwd):
+    """Forward-only calls (no gradients, no logits chunk) on the same inputs:
+    ms per call; its loss must equal the fwd+bwd loss to the bit."""
+    import torch
+
+    dev = Xd.device
+    fwd_out = (torch.empty((), dtype=torch.float32, device=dev), torch.empty((1,), dtype=torch.int32, device=dev))
+    fwd_ws = torch.empty((flce.flce_fwd_workspace_bytes(w.BT, w.H, w.V, 0, w.torch_dtype),), dtype=torch.uint8,
+                         device=dev)
+    for _ in range(2):
+        flce.flce_forward(Xd, Wd, yd, w.ignore_index, 0, out=fwd_out, workspace=fwd_ws, check=False)
+    torch.cuda.synchronize()
+    f0 = torch.cuda.Event(enable_timing=True)
+    f1 = torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    for _ in range(steps):
+        flce.flce_forward(Xd, Wd, yd, w.ignore_index, 0, out=fwd_out, workspace=fwd_ws, check=False)
+    f1.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = f0.elapsed_time(f1) / steps
+    if float(fwd_out[0].item()) != loss_fwd_bwd:
+        raise RuntimeError("forward-only loss differs from the fwd+bwd loss")
+    log(f"[bench] forward only: {fwd_ms:.3f} ms/step")
+    return fwd_ms
 
 
 def copy_calibration(nbytes=256 << 20, reps=3):
@@ -192,6 +224,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="llama3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-forward", action="store_true", help="skip the forward-only timing (context field)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
@@ -206,7 +239,7 @@ def main(argv=None):
     w = si.workload(a.config)
     if a.copy_calibration:
         copy_calibration()
-    r = gpu_bench(w, a.steps, a.warmup)
+    r = gpu_bench(w, a.steps, a.warmup, forward=not a.no_forward)
     tokens_per_s = w.BT / (r["ms"] * 1e-3)
     tflops = 6.0 * w.BT * w.H * w.V / (r["ms"] * 1e-3) / 1e12
     dom, roof = roofline(w, r)
@@ -233,6 +266,9 @@ def main(argv=None):
         "dominant_kernel": dom,
         "roofline": roof,
         "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in r["kernels"].items()},
+        "forward_only": None if r["fwd_ms"] is None else {
+            "ms_per_step": round(r["fwd_ms"], 4), "tokens_per_s": round(w.BT / (r["fwd_ms"] * 1e-3), 1),
+            "tflops": round(2.0 * w.BT * w.H * w.V / (r["fwd_ms"] * 1e-3) / 1e12, 2)},
         "device": {"arch": r["arch"], "cus": r["cus"]},
         "loss": r["loss"],
     }

@@ -91,6 +91,23 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
                  int64_t ignore_index, int64_t chunk_tokens, int dtype, float* loss, float* row_loss, void* dX,
                  float* dW, void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream);
 
+/* Bytes of device workspace flce_fwd needs: per-token and per-tile softmax
+ * statistics only (no logits are stored).  chunk_tokens > 0 sets the tokens
+ * per pass (capped at BT); otherwise a pass takes as many tokens as keep its
+ * statistics (8 bytes per token and 128-wide vocabulary block) within
+ * 256 MiB, capped at BT.  Returns 0 for invalid arguments. */
+size_t flce_fwd_workspace_bytes(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);
+
+/* Fused linear + cross-entropy, forward only (evaluation, no gradients): the
+ * loss of flce_fwd_bwd from the same logits and softmax statistics, without
+ * the in-place gradient and the two backward products; the logits never
+ * leave the GEMM epilogue.  loss and row_loss are bitwise equal to those of
+ * flce_fwd_bwd on the same inputs.  Arguments as for flce_fwd_bwd, with
+ * workspace_bytes >= flce_fwd_workspace_bytes(...). */
+int flce_fwd(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H, int64_t V,
+             int64_t ignore_index, int64_t chunk_tokens, int dtype, float* loss, float* row_loss, void* workspace,
+             size_t workspace_bytes, int32_t* err_flag, void* stream);
+
 /* Bytes of device workspace ce_fwd_bwd_inplace needs (a counter, and BT
  * floats of per-token loss when row_loss is NULL). */
 size_t ce_workspace_bytes(int64_t BT, int64_t V);

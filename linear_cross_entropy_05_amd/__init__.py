@@ -2,6 +2,7 @@
 
 Public API (all GPU-only; the HIP library must be built):
     flce_fwd_bwd(X, W, targets, ignore_index=-100, chunk_tokens=0) -> loss, dX, dW
+    flce_forward(X, W, targets, ignore_index=-100) -> loss   (forward only)
     ce_fwd_bwd_inplace(logits, targets, ignore_index=-100) -> loss
     FusedLinearCrossEntropyLoss(ignore_index=-100)(weight, input, target) -> loss
 """
@@ -12,7 +13,9 @@ from .binding import (  # noqa: F401
     ce_fwd_bwd_inplace,
     ce_workspace_bytes,
     flce_chunk_tokens,
+    flce_forward,
     flce_fwd_bwd,
+    flce_fwd_workspace_bytes,
     flce_workspace_bytes,
     header_functions,
     load_library,

@@ -56,6 +56,10 @@ def _declare(lib):
     lib.flce_workspace_bytes.restype = sz
     lib.flce_fwd_bwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, c.c_int, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.flce_fwd_bwd.restype = c.c_int
+    lib.flce_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, c.c_int]
+    lib.flce_fwd_workspace_bytes.restype = sz
+    lib.flce_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, c.c_int, vp, vp, vp, sz, vp, vp]
+    lib.flce_fwd.restype = c.c_int
     lib.ce_workspace_bytes.argtypes = [i64, i64]
     lib.ce_workspace_bytes.restype = sz
     lib.ce_fwd_bwd_inplace.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, sz, vp, vp]
@@ -173,6 +177,45 @@ def flce_fwd_bwd(X, W, targets, ignore_index: int = -100, chunk_tokens: int = 0,
     return (loss, dX, dW, rl) if row_loss else (loss, dX, dW)
 
 
+def flce_fwd_workspace_bytes(BT: int, H: int, V: int, chunk_tokens: int = 0, dtype=torch.bfloat16) -> int:
+    return int(load_library().flce_fwd_workspace_bytes(BT, H, V, chunk_tokens, _DTYPES[dtype]))
+
+
+def flce_forward(X, W, targets, ignore_index: int = -100, chunk_tokens: int = 0, *, row_loss: bool = False,
+                 check: bool = True, out=None, workspace=None):
+    """Fused linear + cross-entropy, forward only: the loss (fp32 0-d) and,
+    with ``row_loss=True``, the per-token losses, without gradients and
+    without storing logits.  Arguments as for :func:`flce_fwd_bwd`; ``out``
+    may pass preallocated (loss, err) tensors."""
+    lib = load_library()
+    _check_tensor("X", X, ndim=2)
+    _check_tensor("W", W, dtype=X.dtype, ndim=2)
+    _check_tensor("targets", targets, dtype=torch.int64, ndim=1)
+    if X.dtype not in _DTYPES:
+        raise TypeError(f"dtype {X.dtype} not supported (float32, bfloat16)")
+    BT, H = X.shape
+    V = W.shape[0]
+    if W.shape[1] != H or targets.shape[0] != BT:
+        raise ValueError(f"shape mismatch X{tuple(X.shape)} W{tuple(W.shape)} targets{tuple(targets.shape)}")
+    dev = X.device
+    if out is None:
+        loss = torch.empty((), dtype=torch.float32, device=dev)
+        err = torch.empty((1,), dtype=torch.int32, device=dev)
+    else:
+        loss, err = out
+    rl = torch.empty((BT,), dtype=torch.float32, device=dev) if row_loss else None
+    need = lib.flce_fwd_workspace_bytes(BT, H, V, chunk_tokens, _DTYPES[X.dtype])
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    st = lib.flce_fwd(_ptr(X), _ptr(W), _ptr(targets), BT, H, V, ignore_index, chunk_tokens, _DTYPES[X.dtype],
+                      _ptr(loss), _ptr(rl), _ptr(workspace), workspace.numel(), _ptr(err), _stream(dev))
+    if st != 0:
+        raise FlceError(st, "flce_fwd")
+    if check:
+        check_err_flag(err, "flce_fwd")
+    return (loss, rl) if row_loss else loss
+
+
 def ce_fwd_bwd_inplace(logits, targets, ignore_index: int = -100, *, row_loss: bool = False, check: bool = True):
     """Cross-entropy on fp32 logits [BT, V]; overwrites logits with d loss / d logits.
 
@@ -263,4 +306,8 @@ class FusedLinearCrossEntropyLoss(torch.nn.Module):
         self.chunk_tokens = chunk_tokens
 
     def forward(self, weight, inp, target):
-        return _FLCEFunction.apply(weight, inp, target, self.ignore_index, self.chunk_tokens)
+        if torch.is_grad_enabled() and (weight.requires_grad or inp.requires_grad):
+            return _FLCEFunction.apply(weight, inp, target, self.ignore_index, self.chunk_tokens)
+        # no gradient wanted: the forward-only path (no logits chunk, a third of the work)
+        return flce_forward(inp.contiguous(), weight.contiguous(), target.contiguous(), self.ignore_index,
+                            self.chunk_tokens)

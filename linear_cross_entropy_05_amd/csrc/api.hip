@@ -6,6 +6,8 @@
 //   for each chunk of C tokens:  logits+statistics -> lse -> in-place grad
 //                                -> dX rows of the chunk -> dW (+)=
 //   loss = sum of token losses / N
+// The forward-only entry point (flce_fwd) runs the first three steps of the
+// same schedule with no chunk buffer: logits never leave the GEMM epilogue.
 // Only one logits chunk exists at a time ("[論文レビュー] Liger Kernel:
 // Efficient Triton Kernels for LLM Training", 提案手法: chunked FLCE to bound
 // the memory of large-vocabulary logits).
@@ -96,6 +98,41 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
   for (int64_t c0 = 0; c0 < BT; c0 += L.C) {
     const int64_t rows = BT - c0 < L.C ? BT - c0 : L.C;
     if (flce::launch_flce_chunk(L, X, W, targets, ignore_index, c0, rows, ws, rl, dX, dW, c0 == 0, s) != hipSuccess)
+      return FLCE_ERR_LAUNCH;
+  }
+  if (flce::launch_loss_final(rl, BT, nvalid, loss, s) != hipSuccess) return FLCE_ERR_LAUNCH;
+  return FLCE_OK;
+}
+
+size_t flce_fwd_workspace_bytes(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype) {
+  if (BT < 0 || H <= 0 || V <= 0 || (dtype != FLCE_F32 && dtype != FLCE_BF16)) return 0;
+  return flce::make_fwd_layout(BT, H, V, chunk_tokens, dtype).total;
+}
+
+int flce_fwd(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H, int64_t V,
+             int64_t ignore_index, int64_t chunk_tokens, int dtype, float* loss, float* row_loss, void* workspace,
+             size_t workspace_bytes, int32_t* err_flag, void* stream) {
+  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_ERR_DTYPE;
+  if (BT < 0 || H <= 0 || V <= 0 || BT > INT32_MAX || V > INT32_MAX) return FLCE_ERR_ARG;
+  if (!W || !loss || !workspace || !err_flag) return FLCE_ERR_ARG;
+  if (BT > 0 && (!X || !targets)) return FLCE_ERR_ARG;
+  if (H % (dtype == FLCE_BF16 ? 8 : 4) != 0) return FLCE_ERR_SHAPE;
+  if (!aligned(W, 16) || (X && !aligned(X, 16)) || (targets && !aligned(targets, 8)) || !aligned(workspace, 256) ||
+      (row_loss && !aligned(row_loss, 4)))
+    return FLCE_ERR_ALIGN;
+  const flce::Layout L = flce::make_fwd_layout(BT, H, V, chunk_tokens, dtype);
+  if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE;
+  if (current_device_ok() != 1) return FLCE_ERR_DEVICE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* nvalid = reinterpret_cast<int32_t*>(ws + L.off_nvalid);
+  float* rl = row_loss ? row_loss : reinterpret_cast<float*>(ws + L.off_rowloss);
+  if (flce::launch_count_valid(targets, BT, V, ignore_index, nvalid, err_flag, s) != hipSuccess)
+    return FLCE_ERR_LAUNCH;
+  for (int64_t c0 = 0; c0 < BT; c0 += L.C) {
+    const int64_t rows = BT - c0 < L.C ? BT - c0 : L.C;
+    if (flce::launch_fwd_chunk(L, X, W, targets, ignore_index, c0, rows, ws, rl, s) != hipSuccess)
       return FLCE_ERR_LAUNCH;
   }
   if (flce::launch_loss_final(rl, BT, nvalid, loss, s) != hipSuccess) return FLCE_ERR_LAUNCH;

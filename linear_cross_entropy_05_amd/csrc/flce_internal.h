@@ -23,6 +23,8 @@ struct Layout {
 };
 
 Layout make_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);
+// Forward only: no chunk buffer; off_chunk == off_dxpart == total.
+Layout make_fwd_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);
 
 // Kernel kinds, in the order flce_profile_end reports them.
 enum Phase {
@@ -57,6 +59,8 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 hipError_t launch_flce_chunk(const Layout& L, const void* X, const void* W, const int64_t* y, int64_t ignore_index,
                              int64_t c0, int64_t rows, char* ws, float* rowloss, void* dX, float* dW, bool first,
                              hipStream_t s);
+hipError_t launch_fwd_chunk(const Layout& L, const void* X, const void* W, const int64_t* y, int64_t ignore_index,
+                            int64_t c0, int64_t rows, char* ws, float* rowloss, hipStream_t s);
 hipError_t launch_loss_final(const float* rowloss, int64_t BT, const int32_t* nvalid, float* loss, hipStream_t s);
 hipError_t launch_ce_rows(float* logits, const int64_t* y, int64_t BT, int64_t V, int64_t ignore_index,
                           const int32_t* nvalid, float* rowloss, hipStream_t s);

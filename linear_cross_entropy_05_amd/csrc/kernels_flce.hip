@@ -146,7 +146,8 @@ __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
   const bool full = v0 + wy * 128 + 128 <= a.V;
   const int64_t half = 2 * vt + wy;
   const int64_t nrows = a.rows - c0 < kTile ? a.rows - c0 : kTile;
-  const Rsrc zr = make_rsrc(a.z + c0 * a.ldz, nrows * a.ldz * (int64_t)sizeof(T));
+  const bool store_z = a.z != nullptr;  // forward only: statistics, no chunk buffer
+  const Rsrc zr = make_rsrc(store_z ? a.z + c0 * a.ldz : a.W.base, store_z ? nrows * a.ldz * (int64_t)sizeof(T) : 0);
   const uint32_t lane_off = (uint32_t)(((wx * 128 + (lane & 31)) * a.ldz + vw) * (int64_t)sizeof(T));
   const uint32_t row32 = (uint32_t)(32 * a.ldz * (int64_t)sizeof(T));
 #pragma unroll
@@ -173,6 +174,7 @@ __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
     // most of the softmax mass are then small numbers and keep their
     // precision.  Rows are padded to a multiple of 256, so a tile never
     // crosses into the next row; entries past V fill the padding.
+    if (!store_z) continue;
     if constexpr (sizeof(T) == 2) {
       // A lane holds 16-byte pieces of one token row, so direct stores would
       // scatter 32 rows per instruction.  Stage the wave's 32 x 128 block in
@@ -542,6 +544,40 @@ Layout make_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int d
   return L;
 }
 
+Layout make_fwd_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype) {
+  Layout L{};
+  L.BT = BT;
+  L.H = H;
+  L.V = V;
+  L.dtype = dtype;
+  L.esize = dtype == 1 ? 2 : 4;
+  L.ldz = (V + kTile - 1) / kTile * kTile;
+  L.nvt = (V + kTile - 1) / kTile;
+  int64_t C = chunk_tokens;
+  if (C <= 0) {
+    // no logits are kept: a pass is bounded only by its statistics
+    // (8 bytes per token and half tile), at most 256 MiB
+    C = ((int64_t)1 << 28) / (2 * L.nvt * 8);
+  }
+  if (C > BT) C = BT;
+  if (C < 1) C = 1;
+  L.C = C;
+  L.splits = 1;
+  size_t o = 0;
+  L.off_nvalid = o;
+  o = align256(o + 16);
+  L.off_lse = o;
+  o = align256(o + (size_t)C * 4);
+  L.off_rowloss = o;
+  o = align256(o + (size_t)(BT > 0 ? BT : 1) * 4);
+  L.off_part = o;
+  o = align256(o + (size_t)C * 2 * L.nvt * 8);
+  L.off_chunk = o;
+  L.off_dxpart = o;
+  L.total = o;
+  return L;
+}
+
 hipError_t launch_count_valid(const int64_t* y, int64_t BT, int64_t V, int64_t ign, int32_t* nvalid, int32_t* err,
                               hipStream_t s) {
   ProfScope ps(kPhaseCount, s);
@@ -564,18 +600,16 @@ hipError_t launch_loss_final(const float* rowloss, int64_t BT, const int32_t* nv
   return hipGetLastError();
 }
 
+// Logits of one chunk with their softmax statistics (and, when z is not
+// null, the chunk buffer), then lse and the per-token losses.
 template <typename T>
-static hipError_t chunk_impl(const Layout& L, const T* X, const T* W, const int64_t* y, int64_t ign, int64_t c0,
-                             int64_t rows, char* ws, float* rowloss, T* dX, float* dW, bool first, hipStream_t s) {
+static void logits_lse(const Layout& L, const T* X, const T* W, const int64_t* y, int64_t ign, int64_t c0,
+                       int64_t rows, char* ws, float* rowloss, T* z, hipStream_t s) {
   const int64_t H = L.H, V = L.V;
-  T* z = reinterpret_cast<T*>(ws + L.off_chunk);
   float2* part = reinterpret_cast<float2*>(ws + L.off_part);
   float* lse = reinterpret_cast<float*>(ws + L.off_lse);
-  const int32_t* nvalid = reinterpret_cast<const int32_t*>(ws + L.off_nvalid);
   const T* Xc = X + c0 * H;
   const int64_t* yc = y + c0;
-
-  // logits + softmax statistics
   LogitsArgs<T> la;
   la.W = Operand<T>{W, H, V, H};
   la.X = Operand<T>{Xc, H, rows, H};
@@ -598,6 +632,20 @@ static hipError_t chunk_impl(const Layout& L, const T* X, const T* W, const int6
     hipLaunchKernelGGL(k_lse<T>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, part, 2 * L.nvt, Xc, W, H, V, yc,
                        ign, rows, lse, rowloss + c0);
   }
+}
+
+template <typename T>
+static hipError_t chunk_impl(const Layout& L, const T* X, const T* W, const int64_t* y, int64_t ign, int64_t c0,
+                             int64_t rows, char* ws, float* rowloss, T* dX, float* dW, bool first, hipStream_t s) {
+  const int64_t H = L.H, V = L.V;
+  T* z = reinterpret_cast<T*>(ws + L.off_chunk);
+  float2* part = reinterpret_cast<float2*>(ws + L.off_part);
+  float* lse = reinterpret_cast<float*>(ws + L.off_lse);
+  const int32_t* nvalid = reinterpret_cast<const int32_t*>(ws + L.off_nvalid);
+  const T* Xc = X + c0 * H;
+  const int64_t* yc = y + c0;
+
+  logits_lse<T>(L, X, W, y, ign, c0, rows, ws, rowloss, z, s);
   {
     ProfScope ps(kPhaseGrad, s);
     hipLaunchKernelGGL(k_grad<T>, dim3((unsigned)rows), dim3(256), 0, s, z, L.ldz, V, lse, part, 2 * L.nvt, yc, ign,
@@ -646,6 +694,17 @@ static hipError_t chunk_impl(const Layout& L, const T* X, const T* W, const int6
     ProfScope ps(kPhaseDw, s);
     hipLaunchKernelGGL(k_dw<T>, dim3((unsigned)(wa.nvt * wa.nht)), dim3(kThreads), 0, s, wa);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_chunk(const Layout& L, const void* X, const void* W, const int64_t* y, int64_t ign, int64_t c0,
+                            int64_t rows, char* ws, float* rowloss, hipStream_t s) {
+  if (L.dtype == 1)
+    logits_lse<__bf16>(L, static_cast<const __bf16*>(X), static_cast<const __bf16*>(W), y, ign, c0, rows, ws, rowloss,
+                       nullptr, s);
+  else
+    logits_lse<float>(L, static_cast<const float*>(X), static_cast<const float*>(W), y, ign, c0, rows, ws, rowloss,
+                      nullptr, s);
   return hipGetLastError();
 }
 

@@ -21,6 +21,8 @@ def test_exports_every_declared_function(lib):
     names = header_functions()
     assert set(names) >= {
         "flce_fwd_bwd",
+        "flce_fwd",
+        "flce_fwd_workspace_bytes",
         "ce_fwd_bwd_inplace",
         "flce_workspace_bytes",
         "ce_workspace_bytes",
@@ -99,6 +101,53 @@ def _call(lib, **kw):
 def test_host_argument_checks(lib, kw, status):
     # fake, never-dereferenced addresses: every case is rejected on the host
     assert _call(lib, **kw) == status
+
+
+def _call_fwd(lib, **kw):
+    a = dict(X=16, W=16, t=16, BT=8, H=128, V=256, ign=-100, C=0, dt=F32, loss=16, rl=None, ws=256, wsb=1 << 20,
+             err=16, stream=None)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return lib.flce_fwd(vp(a["X"]), vp(a["W"]), vp(a["t"]), a["BT"], a["H"], a["V"], a["ign"], a["C"], a["dt"],
+                        vp(a["loss"]), vp(a["rl"]), vp(a["ws"]), a["wsb"], vp(a["err"]), vp(a["stream"]))
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(dt=5), 2),
+        (dict(H=0), 1),
+        (dict(V=0), 1),
+        (dict(BT=-1), 1),
+        (dict(W=None), 1),
+        (dict(X=None), 1),
+        (dict(t=None), 1),
+        (dict(loss=None), 1),
+        (dict(ws=None), 1),
+        (dict(err=None), 1),
+        (dict(H=130), 7),
+        (dict(H=132, dt=BF16), 7),
+        (dict(X=24), 8),
+        (dict(W=8), 8),
+        (dict(ws=128), 8),
+        (dict(t=20), 8),
+        (dict(rl=18), 8),
+        (dict(wsb=16), 3),
+    ],
+)
+def test_forward_host_argument_checks(lib, kw, status):
+    assert _call_fwd(lib, **kw) == status
+
+
+def test_forward_workspace_has_no_chunk_buffer(lib):
+    # statistics only: 8 bytes per token and 128-wide vocabulary block, plus O(BT)
+    for BT, H, V in ((8192, 4096, 128256), (16384, 3584, 152064), (8192, 3072, 256000)):
+        ws = lib.flce_fwd_workspace_bytes(BT, H, V, 0, BF16)
+        nvh = 2 * ((V + 255) // 256)
+        assert ws <= BT * nvh * 8 + 3 * BT * 4 + 4096, (BT, H, V, ws)
+        assert ws < lib.flce_workspace_bytes(BT, H, V, 0, BF16) / 4
+    assert lib.flce_fwd_workspace_bytes(8, 0, 256, 0, F32) == 0
+    assert lib.flce_fwd_workspace_bytes(8, 128, 256, 0, 9) == 0
 
 
 def test_ce_host_argument_checks(lib):

@@ -8,6 +8,8 @@ FLCE heads (Llama-3-8B, Qwen2-7B at 16K context, Gemma 256K vocabulary):
     4096 + 4 H dW entries (including the rows of the most frequent targets);
   * against the oracle computed here, one token at a time (flce_rows_ref):
     full dX rows and per-token losses of 6 tokens.
+Forward only (flce_fwd) on the same three heads: the loss and the 64 stored
+token losses.
 Logits-only cross-entropy on the Gemma shape (fp32 logits 8192 x 256000,
 8.4 GB): per-token losses of every row and the loss from the per-row oracle,
 full dlogits rows for 16 sampled tokens.
@@ -68,6 +70,28 @@ def test_flce_full_size(name):
     er2 = rel_err(to_np(rl[torch.tensor(pick, device=dev)]), ref["row_loss"])
     say(f"  per-row oracle: dX rows {ex2:.2e}; token losses {er2:.2e}")
     assert ex2 <= tg and er2 <= tl
+
+
+@pytest.mark.parametrize("name", ["llama3", "qwen2", "gemma"])
+def test_flce_forward_full_size(name):
+    """Forward only, automatic pass size: the loss and 64 token losses
+    against the stored oracle values."""
+    import linear_cross_entropy_05_amd as flce
+
+    with open(os.path.join(GOLDEN, f"{name}.json")) as f:
+        g = json.load(f)
+    w = si.workload(name)
+    X, W, y = si.make_inputs(w)
+    assert si.fingerprint(X, W, y) == g["fingerprint"], "seeded inputs differ from the ones the oracle saw"
+    dev = torch.device("cuda", 0)
+    say(f"[gpu] flce_forward {name} BT={w.BT} H={w.H} V={w.V} chunk=auto")
+    loss, rl = flce.flce_forward(X.to(dev), W.to(dev), y.to(dev), w.ignore_index, row_loss=True)
+    torch.cuda.synchronize()
+    tl, _ = TOL[w.dtype]
+    el = abs(loss.item() - g["loss"]) / abs(g["loss"])
+    er = rel_err(to_np(rl[torch.tensor(g["rows"], device=dev)]), g["row_loss"])
+    say(f"  loss {loss.item():.7f} ref {g['loss']:.7f} err {el:.2e}; rows {er:.2e}")
+    assert el <= tl and er <= tl
 
 
 def test_ce_inplace_gemma_shape():
