@@ -118,6 +118,10 @@ __device__ __forceinline__ void store4_ptr(float* p, float a, float b, float c, 
   *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
 }
 
+// Stand-in logit for vocabulary entries past V in the last tile: below any
+// real logit, finite, and a power of two (so m * log2e is exact for it)
+constexpr float kPad = -0x1p100f;
+
 // LDS row pitch (bytes) of the staged bf16 chunk block in the logits epilogue
 constexpr int kZPitch = 264;
 // cache-policy bits of a buffer store that streams past the L2 (nt): the chunk
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
   f32x16 acc[4][4];
   gemm_mainloop<T, false, false>(smem, a.W, v0, a.X, c0, 0, a.H, acc);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wy = wave >> 1, wx = wave & 1;
   // accumulator (i, j, e) holds Z[c, v] with
   //   v = vw + 32 i + 8 (e / 4) + e % 4,  c = cw + 32 j + lane % 32
@@ -150,24 +154,36 @@ __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
   const Rsrc zr = make_rsrc(store_z ? a.z + c0 * a.ldz : a.W.base, store_z ? nrows * a.ldz * (int64_t)sizeof(T) : 0);
   const uint32_t lane_off = (uint32_t)(((wx * 128 + (lane & 31)) * a.ldz + vw) * (int64_t)sizeof(T));
   const uint32_t row32 = (uint32_t)(32 * a.ldz * (int64_t)sizeof(T));
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // max over the 128 entries of token c: 64 in this lane, 64 in lane ^ 32
-    float m = -FLT_MAX;
+  if (!full) {
+    // Entries past V (zero rows of W) must not count.  Pushed far below any
+    // logit they add exp(kPad - m) = 0 to a block's sum; a block with no
+    // entry below V gets (M_h, s_h) = (kPad, 0), which the lse combine
+    // weighs by exp(M_h - M) = 0, and the gradient pass zeroes those columns.
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (full || vw + 32 * i + 8 * (e >> 2) + (e & 3) < a.V) m = fmaxf(m, acc[i][j][e]);
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (vw + 32 * i + 8 * (e >> 2) + (e & 3) >= a.V) acc[i][j][e] = kPad;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // max over the 128 entries of token c: 64 in this lane, 64 in lane ^ 32
+    float m = acc[0][j][0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) m = fmaxf(m, acc[i][j][e]);
     m = fmaxf(m, __shfl_xor(m, 32));
     const float mb = m * kLog2e;
     float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (full || vw + 32 * i + 8 * (e >> 2) + (e & 3) < a.V) sum += exp2_fast(fmaf(acc[i][j][e], kLog2e, -mb));
+      for (int e = 0; e < 16; ++e) sum += exp2_fast(fmaf(acc[i][j][e], kLog2e, -mb));
     sum += __shfl_xor(sum, 32);
+    if (m == kPad) sum = 0.f;  // no entry of this block lies below V
     const int64_t c = cw + 32 * j;
     if (lane < 32 && c < a.rows) a.part[c * a.nvh + half] = float2{m, sum};
     // z - m, rounded to the chunk's element type: the entries that carry
