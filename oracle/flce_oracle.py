@@ -101,11 +101,14 @@ def ce_ref(logits, y, ignore_index: int = -100):
     return _ce(np.array(_as_f64(logits), dtype=np.float64, copy=True), y, ignore_index)
 
 
-def _ce(Z: np.ndarray, y, ignore_index: int, n_valid=None):
+def _ce(Z: np.ndarray, y, ignore_index: int, n_valid=None, token_scale=None):
     """ce_ref on a float64 logits array it overwrites (Z becomes dlogits).
 
     ``n_valid`` overrides N (the count of non-ignored rows) when Z holds only
-    some rows of a larger batch.
+    some rows of a larger batch.  ``token_scale`` [BT], when given, replaces
+    the 1/N factor of each row's gradient: dlogits_i = (softmax_i - onehot_i)
+    * token_scale[i], the gradient of sum_i token_scale[i] * loss_i (the loss
+    itself stays the mean).
     """
     y = _as_i64(y)
     BT, V = Z.shape
@@ -127,7 +130,10 @@ def _ce(Z: np.ndarray, y, ignore_index: int, n_valid=None):
     Z /= s[:, None]
     Z[rows[keep], y[keep]] -= 1.0
     Z[~keep, :] = 0.0
-    Z /= denom
+    if token_scale is None:
+        Z /= denom
+    else:
+        Z *= np.asarray(token_scale, dtype=np.float64).reshape(BT, 1)
     return {"loss": loss, "dlogits": Z, "row_loss": row_loss, "lse": lse, "n_valid": n}
 
 
@@ -145,19 +151,22 @@ def ce_rows_ref(logits_rows, y_rows, n_valid: int, ignore_index: int = -100):
     return out
 
 
-def flce_ref(X, W, y, ignore_index: int = -100):
+def flce_ref(X, W, y, ignore_index: int = -100, token_scale=None):
     """Fused linear + cross-entropy, forward and backward, by the plain definition.
 
     X [BT, H], W [V, H] (nn.Linear weight layout, no bias), y [BT] integer.
     Returns a dict with ``loss``, ``dX`` [BT, H], ``dW`` [V, H], ``row_loss``,
     ``lse``, ``n_valid`` and the full ``dlogits`` [BT, V], all float64.
+    With ``token_scale`` [BT] the gradients are those of
+    sum_i token_scale[i] * loss_i instead of the mean (see ``_ce``).
     """
     X64 = _as_f64(X)
     W64 = _as_f64(W)
     if X64.ndim != 2 or W64.ndim != 2 or X64.shape[1] != W64.shape[1]:
         raise ValueError(f"shape mismatch X{X64.shape} W{W64.shape}")
     Z = X64 @ W64.T
-    out = _ce(Z, y, ignore_index)  # Z is overwritten by dlogits
+    ts = None if token_scale is None else _as_f64(token_scale)
+    out = _ce(Z, y, ignore_index, token_scale=ts)  # Z is overwritten by dlogits
     G = out["dlogits"]
     out["dX"] = G @ W64
     out["dW"] = G.T @ X64

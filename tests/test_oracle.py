@@ -101,3 +101,65 @@ def test_ce_rows_ref_matches_full_batch():
 def test_row_lse_closed_form():
     Z = np.log(np.array([[1.0, 2.0, 3.0, 4.0], [0.5, 0.5, 0.5, 0.5]]))
     assert np.allclose(oracle.row_lse(Z), [np.log(10.0), np.log(2.0)], rtol=1e-15)
+
+
+# ---- per-token gradient scales (token_scale): gradients of sum_i s_i * loss_i ----
+
+def _weighted_case(seed, BT=6, H=4, V=7):
+    r = np.random.default_rng(seed)
+    X = r.standard_normal((BT, H))
+    W = r.standard_normal((V, H)) * 0.4
+    y = r.integers(0, V, BT)
+    y[2] = -100
+    s = r.uniform(-1.0, 2.0, BT)  # any real weights, negative ones included
+    return X, W, y, s
+
+
+def test_token_scale_finite_differences():
+    """dX and dW with token_scale s are the central differences of
+    f = sum_i s_i * loss_i, where loss_i are the oracle's token losses (pinned
+    on their own by the definition pins)."""
+    X, W, y, s = _weighted_case(41)
+    out = oracle.flce_ref(X, W, y, -100, token_scale=s)
+    h = 1e-6
+
+    def f(Xa, Wa):
+        return float(np.dot(s, oracle.flce_ref(Xa, Wa, y, -100)["row_loss"]))
+
+    for name, A in (("dX", X), ("dW", W)):
+        num = np.zeros_like(A)
+        for i in range(A.shape[0]):
+            for j in range(A.shape[1]):
+                P, M = A.copy(), A.copy()
+                P[i, j] += h
+                M[i, j] -= h
+                num[i, j] = (f(P, W) - f(M, W)) / (2 * h) if name == "dX" else (f(X, P) - f(X, M)) / (2 * h)
+        err = float(np.max(np.abs(out[name] - num))) / float(np.max(np.abs(num)))
+        assert err <= 1e-7, (name, err)
+    # the loss itself is still the mean over non-ignored tokens
+    assert out["loss"] == oracle.flce_ref(X, W, y, -100)["loss"]
+
+
+def test_token_scale_against_torch():
+    """torch CPU float64: cross_entropy(reduction='none') weighted by s, summed, autograd."""
+    import torch
+    import torch.nn.functional as F
+
+    X, W, y, s = _weighted_case(42, BT=9, H=5, V=11)
+    Xt = torch.tensor(X, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    rows = F.cross_entropy(Xt @ Wt.T, torch.tensor(y), ignore_index=-100, reduction="none")
+    (rows * torch.tensor(s)).sum().backward()
+    out = oracle.flce_ref(X, W, y, -100, token_scale=s)
+    assert float(np.max(np.abs(out["dX"] - Xt.grad.numpy()))) <= 1e-12 * float(np.max(np.abs(Xt.grad.numpy())))
+    assert float(np.max(np.abs(out["dW"] - Wt.grad.numpy()))) <= 1e-12 * float(np.max(np.abs(Wt.grad.numpy())))
+    assert np.allclose(out["row_loss"], rows.detach().numpy(), rtol=1e-13, atol=0)
+
+
+def test_token_scale_one_over_n_is_the_mean():
+    X, W, y, _ = _weighted_case(43)
+    n = int((y != -100).sum())
+    a = oracle.flce_ref(X, W, y, -100)
+    b = oracle.flce_ref(X, W, y, -100, token_scale=np.full(len(y), 1.0 / n))
+    assert float(np.max(np.abs(a["dX"] - b["dX"]))) <= 1e-15 * float(np.max(np.abs(a["dX"])))
+    assert float(np.max(np.abs(a["dW"] - b["dW"]))) <= 1e-15 * float(np.max(np.abs(a["dW"])))
