@@ -80,16 +80,24 @@ size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, int64_t chunk_toke
  *   X        [BT, H] dtype, 16-byte aligned        (may be NULL if BT == 0)
  *   W        [V, H]  dtype, 16-byte aligned
  *   targets  [BT]    int64, values in [0, V) or ignore_index
+ *   token_scale [BT] float or NULL: NULL gives the gradients of the mean
+ *            loss (factor 1/N per token); otherwise token i's gradient rows
+ *            are (softmax - onehot) * token_scale[i], the gradients of
+ *            sum_i token_scale[i] * l_i (reduction "none" or "sum" with an
+ *            upstream gradient; ignored tokens stay 0).  The loss output is
+ *            the mean either way.  4-byte aligned.
  *   loss     device float scalar: sum of token losses / N (0 when N == 0)
  *   row_loss [BT] float or NULL: per-token loss l_i (0 on ignored tokens)
  *   dX       [BT, H] dtype: d loss / d X          (may be NULL if BT == 0)
  *   dW       [V, H]  float: d loss / d W, fp32 (overwritten, not accumulated into)
  *   workspace, workspace_bytes: >= flce_workspace_bytes(...), 256-byte aligned
  *   err_flag device int32: 0, or FLCE_ERR_TARGET after the call completes
- * Gradients are for an upstream gradient of 1; scale them for another. */
-int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H, int64_t V,
-                 int64_t ignore_index, int64_t chunk_tokens, int dtype, float* loss, float* row_loss, void* dX,
-                 float* dW, void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream);
+ * With token_scale NULL the gradients are for an upstream gradient of 1 on the
+ * mean loss; scale them for another. */
+int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, const float* token_scale, int64_t BT,
+                 int64_t H, int64_t V, int64_t ignore_index, int64_t chunk_tokens, int dtype, float* loss,
+                 float* row_loss, void* dX, float* dW, void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                 void* stream);
 
 /* Bytes of device workspace flce_fwd needs: per-token and per-tile softmax
  * statistics only (no logits are stored).  chunk_tokens > 0 sets the tokens

@@ -54,7 +54,7 @@ def _declare(lib):
     lib.flce_chunk_tokens.restype = i64
     lib.flce_workspace_bytes.argtypes = [i64, i64, i64, i64, c.c_int]
     lib.flce_workspace_bytes.restype = sz
-    lib.flce_fwd_bwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, c.c_int, vp, vp, vp, vp, vp, sz, vp, vp]
+    lib.flce_fwd_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, c.c_int, vp, vp, vp, vp, vp, sz, vp, vp]
     lib.flce_fwd_bwd.restype = c.c_int
     lib.flce_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, c.c_int]
     lib.flce_fwd_workspace_bytes.restype = sz
@@ -134,21 +134,28 @@ def check_err_flag(err: torch.Tensor, what: str):
         raise FlceError(v, what)
 
 
-def flce_fwd_bwd(X, W, targets, ignore_index: int = -100, chunk_tokens: int = 0, *, row_loss: bool = False,
-                 check: bool = True, out=None, workspace=None):
+def flce_fwd_bwd(X, W, targets, ignore_index: int = -100, chunk_tokens: int = 0, *, token_scale=None,
+                 row_loss: bool = False, check: bool = True, out=None, workspace=None):
     """Fused linear + cross-entropy forward and backward.
 
     X [BT, H] and W [V, H] (fp32 or bf16, same dtype), targets [BT] int64.
     Returns (loss fp32 0-d, dX [BT, H] X.dtype, dW [V, H] fp32) and, with
-    ``row_loss=True``, the per-token losses [BT] fp32.  With ``check`` the
-    call synchronises and raises if a target was out of range.  ``out`` may
-    pass preallocated (loss, dX, dW, err) tensors and ``workspace`` a uint8
-    device tensor, to keep allocations out of timed loops.
+    ``row_loss=True``, the per-token losses [BT] fp32.  ``token_scale``
+    (fp32 [BT], optional) makes the gradients those of
+    sum_i token_scale[i] * loss_i instead of the mean; the returned loss is
+    the mean either way.  With ``check`` the call synchronises and raises if
+    a target was out of range.  ``out`` may pass preallocated (loss, dX, dW,
+    err) tensors and ``workspace`` a uint8 device tensor, to keep
+    allocations out of timed loops.
     """
     lib = load_library()
     _check_tensor("X", X, ndim=2)
     _check_tensor("W", W, dtype=X.dtype, ndim=2)
     _check_tensor("targets", targets, dtype=torch.int64, ndim=1)
+    if token_scale is not None:
+        _check_tensor("token_scale", token_scale, dtype=torch.float32, ndim=1)
+        if token_scale.shape[0] != X.shape[0]:
+            raise ValueError("token_scale length must equal the number of tokens")
     if X.dtype not in _DTYPES:
         raise TypeError(f"dtype {X.dtype} not supported (float32, bfloat16)")
     BT, H = X.shape
@@ -168,8 +175,8 @@ def flce_fwd_bwd(X, W, targets, ignore_index: int = -100, chunk_tokens: int = 0,
     if workspace is None:
         workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
     st = lib.flce_fwd_bwd(
-        _ptr(X), _ptr(W), _ptr(targets), BT, H, V, ignore_index, chunk_tokens, _DTYPES[X.dtype], _ptr(loss),
-        _ptr(rl), _ptr(dX), _ptr(dW), _ptr(workspace), workspace.numel(), _ptr(err), _stream(dev))
+        _ptr(X), _ptr(W), _ptr(targets), _ptr(token_scale), BT, H, V, ignore_index, chunk_tokens, _DTYPES[X.dtype],
+        _ptr(loss), _ptr(rl), _ptr(dX), _ptr(dW), _ptr(workspace), workspace.numel(), _ptr(err), _stream(dev))
     if st != 0:
         raise FlceError(st, "flce_fwd_bwd")
     if check:
@@ -276,8 +283,9 @@ class KernelTimer:
 
 
 class _FLCEFunction(torch.autograd.Function):
-    """Forward computes the loss and both gradients at once (one pass over the
-    chunks); backward scales the stored gradients by the upstream gradient."""
+    """Mean reduction.  Forward computes the loss and both gradients at once
+    (one pass over the chunks); backward hands them on, scaled by the
+    upstream gradient unless that is exactly 1."""
 
     @staticmethod
     def forward(ctx, weight, inp, target, ignore_index, chunk_tokens):
@@ -290,23 +298,61 @@ class _FLCEFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, grad):
         dX, dW = ctx.saved_tensors
+        if bool(torch.equal(grad, torch.ones_like(grad))):
+            gx = dX if ctx.needs_input_grad[1] else None
+            gw = dW.to(ctx.weight_dtype) if ctx.needs_input_grad[0] else None
+            return gw, gx, None, None, None
         g = grad.to(torch.float32)
         gx = (dX.float() * g).to(dX.dtype) if ctx.needs_input_grad[1] else None
         gw = (dW * g).to(ctx.weight_dtype) if ctx.needs_input_grad[0] else None
         return gw, gx, None, None, None
 
 
-class FusedLinearCrossEntropyLoss(torch.nn.Module):
-    """``loss = FusedLinearCrossEntropyLoss()(weight, input, target)``: mean
-    cross-entropy of ``input @ weight.T`` over targets != ignore_index."""
+class _FLCETokenFunction(torch.autograd.Function):
+    """No reduction: forward returns the per-token losses (forward-only path,
+    no logits kept); backward runs the fused pass with the upstream per-token
+    gradients as the token scales."""
 
-    def __init__(self, ignore_index: int = -100, chunk_tokens: int = 0):
+    @staticmethod
+    def forward(ctx, weight, inp, target, ignore_index, chunk_tokens):
+        weight, inp, target = weight.contiguous(), inp.contiguous(), target.contiguous()
+        _, rl = flce_forward(inp, weight, target, ignore_index, chunk_tokens, row_loss=True)
+        ctx.save_for_backward(weight, inp, target)
+        ctx.ignore_index, ctx.chunk_tokens = ignore_index, chunk_tokens
+        return rl
+
+    @staticmethod
+    def backward(ctx, grad_rows):
+        weight, inp, target = ctx.saved_tensors
+        scale = grad_rows.to(torch.float32).contiguous()
+        _, dX, dW = flce_fwd_bwd(inp, weight, target, ctx.ignore_index, ctx.chunk_tokens, token_scale=scale)
+        gx = dX if ctx.needs_input_grad[1] else None
+        gw = dW.to(weight.dtype) if ctx.needs_input_grad[0] else None
+        return gw, gx, None, None, None
+
+
+class FusedLinearCrossEntropyLoss(torch.nn.Module):
+    """``loss = FusedLinearCrossEntropyLoss()(weight, input, target)``:
+    cross-entropy of ``input @ weight.T`` over targets != ignore_index, as
+    the mean (``reduction="mean"``) or per token (``reduction="none"``, 0 on
+    ignored tokens)."""
+
+    def __init__(self, ignore_index: int = -100, chunk_tokens: int = 0, reduction: str = "mean"):
         super().__init__()
+        if reduction not in ("mean", "none"):
+            raise ValueError(f"reduction must be 'mean' or 'none', got {reduction!r}")
         self.ignore_index = ignore_index
         self.chunk_tokens = chunk_tokens
+        self.reduction = reduction
 
     def forward(self, weight, inp, target):
-        if torch.is_grad_enabled() and (weight.requires_grad or inp.requires_grad):
+        grad = torch.is_grad_enabled() and (weight.requires_grad or inp.requires_grad)
+        if self.reduction == "none":
+            if grad:
+                return _FLCETokenFunction.apply(weight, inp, target, self.ignore_index, self.chunk_tokens)
+            return flce_forward(inp.contiguous(), weight.contiguous(), target.contiguous(), self.ignore_index,
+                                self.chunk_tokens, row_loss=True)[1]
+        if grad:
             return _FLCEFunction.apply(weight, inp, target, self.ignore_index, self.chunk_tokens)
         # no gradient wanted: the forward-only path (no logits chunk, a third of the work)
         return flce_forward(inp.contiguous(), weight.contiguous(), target.contiguous(), self.ignore_index,

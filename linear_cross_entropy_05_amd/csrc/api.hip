@@ -70,16 +70,18 @@ size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, int64_t chunk_toke
   return flce::make_layout(BT, H, V, chunk_tokens, dtype).total;
 }
 
-int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H, int64_t V,
-                 int64_t ignore_index, int64_t chunk_tokens, int dtype, float* loss, float* row_loss, void* dX,
-                 float* dW, void* workspace, size_t workspace_bytes, int32_t* err_flag, void* stream) {
+int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, const float* token_scale, int64_t BT,
+                 int64_t H, int64_t V, int64_t ignore_index, int64_t chunk_tokens, int dtype, float* loss,
+                 float* row_loss, void* dX, float* dW, void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                 void* stream) {
   if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_ERR_DTYPE;
   if (BT < 0 || H <= 0 || V <= 0 || BT > INT32_MAX || V > INT32_MAX) return FLCE_ERR_ARG;
   if (!W || !loss || !dW || !workspace || !err_flag) return FLCE_ERR_ARG;
   if (BT > 0 && (!X || !targets || !dX)) return FLCE_ERR_ARG;
   if (H % (dtype == FLCE_BF16 ? 8 : 4) != 0) return FLCE_ERR_SHAPE;
   if (!aligned(W, 16) || (X && !aligned(X, 16)) || (targets && !aligned(targets, 8)) || !aligned(workspace, 256) ||
-      !aligned(dW, 4) || (dX && !aligned(dX, dtype == FLCE_BF16 ? 2 : 4)) || (row_loss && !aligned(row_loss, 4)))
+      !aligned(dW, 4) || (dX && !aligned(dX, dtype == FLCE_BF16 ? 2 : 4)) || (row_loss && !aligned(row_loss, 4)) ||
+      (token_scale && !aligned(token_scale, 4)))
     return FLCE_ERR_ALIGN;
   const flce::Layout L = flce::make_layout(BT, H, V, chunk_tokens, dtype);
   if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE;
@@ -97,7 +99,8 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, int64_t B
   }
   for (int64_t c0 = 0; c0 < BT; c0 += L.C) {
     const int64_t rows = BT - c0 < L.C ? BT - c0 : L.C;
-    if (flce::launch_flce_chunk(L, X, W, targets, ignore_index, c0, rows, ws, rl, dX, dW, c0 == 0, s) != hipSuccess)
+    if (flce::launch_flce_chunk(L, X, W, targets, token_scale, ignore_index, c0, rows, ws, rl, dX, dW, c0 == 0, s) !=
+        hipSuccess)
       return FLCE_ERR_LAUNCH;
   }
   if (flce::launch_loss_final(rl, BT, nvalid, loss, s) != hipSuccess) return FLCE_ERR_LAUNCH;

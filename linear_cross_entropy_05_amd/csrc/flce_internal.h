@@ -56,9 +56,10 @@ class ProfScope {
 hipError_t launch_count_valid(const int64_t* y, int64_t BT, int64_t V, int64_t ignore_index, int32_t* nvalid,
                               int32_t* err, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
-hipError_t launch_flce_chunk(const Layout& L, const void* X, const void* W, const int64_t* y, int64_t ignore_index,
-                             int64_t c0, int64_t rows, char* ws, float* rowloss, void* dX, float* dW, bool first,
-                             hipStream_t s);
+// scale: NULL (gradient factor 1/N) or per-token gradient factors [BT]
+hipError_t launch_flce_chunk(const Layout& L, const void* X, const void* W, const int64_t* y, const float* scale,
+                             int64_t ignore_index, int64_t c0, int64_t rows, char* ws, float* rowloss, void* dX,
+                             float* dW, bool first, hipStream_t s);
 hipError_t launch_fwd_chunk(const Layout& L, const void* X, const void* W, const int64_t* y, int64_t ignore_index,
                             int64_t c0, int64_t rows, char* ws, float* rowloss, hipStream_t s);
 hipError_t launch_loss_final(const float* rowloss, int64_t BT, const int32_t* nvalid, float* loss, hipStream_t s);

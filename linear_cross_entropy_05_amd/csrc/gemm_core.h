@@ -503,71 +503,109 @@ __device__ __forceinline__ void mma_step(const u32x4 (&fa)[4], const u32x4 (&fb)
     for (int j = 0; j < 4; ++j) acc[i][j] = mma_chunk<__bf16>(fa[i], fb[j], acc[i][j]);
 }
 
+// One tile's pass over K, split so that a persistent kernel can start the
+// copies of its next tile (init + prologue) before the epilogue of the
+// current one.  run() expects prologue() to have been issued by this
+// workgroup and ends with a barrier after which the stage buffers are free.
+template <bool kAKMajor, bool kBKMajor>
+struct Pipe {
+  LoaderT<kAKMajor> la;
+  LoaderT<kBKMajor> lb;
+  int64_t k0;
+  int nk;
+
+  __device__ __forceinline__ void init(const Operand<__bf16>& A, int64_t m0, const Operand<__bf16>& B, int64_t n0,
+                                       int64_t k0_, int64_t k1) {
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    k0 = k0_;
+    nk = (int)((k1 - k0 + kBK - 1) / kBK);
+    if (nk < 0) nk = 0;
+    la.init(A, m0, wave, lane);
+    lb.init(B, n0, wave, lane);
+  }
+
+  // copies of stages 0 and 1 into buffers 0 and 1 (no wait)
+  __device__ __forceinline__ void prologue(uint32_t lds0) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (nk > 0) {
+      la.issue(lds0, k0, wave);
+      lb.issue(lds0 + kOp, k0, wave);
+    }
+    if (nk > 1) {
+      la.issue(lds0 + kStage, k0 + kBK, wave);
+      lb.issue(lds0 + kStage + kOp, k0 + kBK, wave);
+    }
+  }
+
+  // `pending`: copies this wave issued after the prologue and before run()
+  // (they complete after it, so the first wait leaves them in flight)
+  template <int kPending = 0>
+  __device__ __forceinline__ void run(char* smem, f32x16 (&acc)[4][4]) const {
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wy = wave >> 1, wx = wave & 1;
+    const uint32_t lds0 = lds_addr(smem);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    if (nk <= 0) {
+      wait_vm<0>();
+      __syncthreads();
+      return;
+    }
+    if (nk > 1)
+      wait_vm<2 * kLoads + kPending>();
+    else
+      wait_vm<kPending>();
+    __syncthreads();
+
+    u32x4 fa[2][4], fb[2][4];
+    load_step<kAKMajor, kBKMajor>(la, lb, smem, 0, wy, wx, lane, fa[0], fb[0]);
+    // every iteration of this loop has a next stage; the last stage follows
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      const char* cur = smem + (kt & 1) * kStage;
+#pragma unroll
+      for (int s = 0; s < 3; ++s) {
+        load_step<kAKMajor, kBKMajor>(la, lb, cur, s + 1, wy, wx, lane, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+        // keep these reads ahead of the MFMAs below
+        __builtin_amdgcn_sched_barrier(0);
+        mma_step(fa[s & 1], fb[s & 1], acc);
+      }
+      // stage kt + 1 landed (this wave's copies), then everyone's; nobody
+      // reads stage kt any more
+      wait_vm<0>();
+      __syncthreads();
+      if (kt + 2 < nk) {
+        const uint32_t dst = lds0 + (kt & 1) * kStage;
+        la.issue(dst, k0 + (int64_t)(kt + 2) * kBK, wave);
+        lb.issue(dst + kOp, k0 + (int64_t)(kt + 2) * kBK, wave);
+      }
+      load_step<kAKMajor, kBKMajor>(la, lb, smem + ((kt + 1) & 1) * kStage, 0, wy, wx, lane, fa[0], fb[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_step(fa[1], fb[1], acc);
+    }
+    {
+      const char* cur = smem + ((nk - 1) & 1) * kStage;
+#pragma unroll
+      for (int s = 0; s < 3; ++s) {
+        load_step<kAKMajor, kBKMajor>(la, lb, cur, s + 1, wy, wx, lane, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_step(fa[s & 1], fb[s & 1], acc);
+      }
+      mma_step(fa[1], fb[1], acc);
+    }
+    wait_vm<0>();
+    __syncthreads();  // stage buffers free
+  }
+};
+
 template <bool kAKMajor, bool kBKMajor>
 __device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, int64_t m0, const Operand<__bf16>& B,
                                          int64_t n0, int64_t k0, int64_t k1, f32x16 (&acc)[4][4]) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wy = wave >> 1, wx = wave & 1;
-  const int nk = (int)((k1 - k0 + kBK - 1) / kBK);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-  if (nk <= 0) return;
-
-  LoaderT<kAKMajor> la;
-  LoaderT<kBKMajor> lb;
-  la.init(A, m0, wave, lane);
-  lb.init(B, n0, wave, lane);
-  const uint32_t lds0 = lds_addr(smem);
-  la.issue(lds0, k0, wave);
-  lb.issue(lds0 + kOp, k0, wave);
-  if (nk > 1) {
-    la.issue(lds0 + kStage, k0 + kBK, wave);
-    lb.issue(lds0 + kStage + kOp, k0 + kBK, wave);
-    wait_vm<2 * kLoads>();
-  } else {
-    wait_vm<0>();
-  }
-  __syncthreads();
-
-  u32x4 fa[2][4], fb[2][4];
-  load_step<kAKMajor, kBKMajor>(la, lb, smem, 0, wy, wx, lane, fa[0], fb[0]);
-  // every iteration of this loop has a next stage; the last stage follows
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    const char* cur = smem + (kt & 1) * kStage;
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      load_step<kAKMajor, kBKMajor>(la, lb, cur, s + 1, wy, wx, lane, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-      // keep these reads ahead of the MFMAs below
-      __builtin_amdgcn_sched_barrier(0);
-      mma_step(fa[s & 1], fb[s & 1], acc);
-    }
-    // stage kt + 1 landed (this wave's copies), then everyone's; nobody
-    // reads stage kt any more
-    wait_vm<0>();
-    __syncthreads();
-    if (kt + 2 < nk) {
-      const uint32_t dst = lds0 + (kt & 1) * kStage;
-      la.issue(dst, k0 + (int64_t)(kt + 2) * kBK, wave);
-      lb.issue(dst + kOp, k0 + (int64_t)(kt + 2) * kBK, wave);
-    }
-    load_step<kAKMajor, kBKMajor>(la, lb, smem + ((kt + 1) & 1) * kStage, 0, wy, wx, lane, fa[0], fb[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    mma_step(fa[1], fb[1], acc);
-  }
-  {
-    const char* cur = smem + ((nk - 1) & 1) * kStage;
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      load_step<kAKMajor, kBKMajor>(la, lb, cur, s + 1, wy, wx, lane, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      mma_step(fa[s & 1], fb[s & 1], acc);
-    }
-    mma_step(fa[1], fb[1], acc);
-  }
-  __syncthreads();  // LDS free for the epilogue
+  Pipe<kAKMajor, kBKMajor> p;
+  p.init(A, m0, B, n0, k0, k1);
+  p.prologue(lds_addr(smem));
+  p.run(smem, acc);
 }
 
 }  // namespace pipe

@@ -298,7 +298,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_grad(T* __restrict__ z, int64_t ldz, int64_t V,
                                               const float* __restrict__ lse, const float2* __restrict__ part,
                                               int64_t nvh, const int64_t* __restrict__ y, int64_t ign,
-                                              const int32_t* __restrict__ nvalid) {
+                                              const int32_t* __restrict__ nvalid, const float* __restrict__ scale) {
   constexpr int E = Elem<T>::chunk;
   const int64_t c = blockIdx.x;
   const int64_t t = y[c];
@@ -308,8 +308,14 @@ __global__ __launch_bounds__(256) void k_grad(T* __restrict__ z, int64_t ldz, in
       *reinterpret_cast<u32x4*>(row + v) = u32x4{0, 0, 0, 0};
     return;
   }
-  const int n = *nvalid;
-  const float inv = 1.f / (float)(n > 0 ? n : 1);
+  // the row's factor: 1/N for the mean, or the caller's per-token scale
+  float inv;
+  if (scale) {
+    inv = scale[c];
+  } else {
+    const int n = *nvalid;
+    inv = 1.f / (float)(n > 0 ? n : 1);
+  }
   const float l = lse[c];
   const float2* pc = part + c * nvh;
   for (int64_t v = (int64_t)threadIdx.x * E; v < ldz; v += 256 * E) {
@@ -651,8 +657,9 @@ static void logits_lse(const Layout& L, const T* X, const T* W, const int64_t* y
 }
 
 template <typename T>
-static hipError_t chunk_impl(const Layout& L, const T* X, const T* W, const int64_t* y, int64_t ign, int64_t c0,
-                             int64_t rows, char* ws, float* rowloss, T* dX, float* dW, bool first, hipStream_t s) {
+static hipError_t chunk_impl(const Layout& L, const T* X, const T* W, const int64_t* y, const float* scale,
+                             int64_t ign, int64_t c0, int64_t rows, char* ws, float* rowloss, T* dX, float* dW,
+                             bool first, hipStream_t s) {
   const int64_t H = L.H, V = L.V;
   T* z = reinterpret_cast<T*>(ws + L.off_chunk);
   float2* part = reinterpret_cast<float2*>(ws + L.off_part);
@@ -665,7 +672,7 @@ static hipError_t chunk_impl(const Layout& L, const T* X, const T* W, const int6
   {
     ProfScope ps(kPhaseGrad, s);
     hipLaunchKernelGGL(k_grad<T>, dim3((unsigned)rows), dim3(256), 0, s, z, L.ldz, V, lse, part, 2 * L.nvt, yc, ign,
-                       nvalid);
+                       nvalid, scale ? scale + c0 : nullptr);
   }
 
   // dX = G W
@@ -724,12 +731,13 @@ hipError_t launch_fwd_chunk(const Layout& L, const void* X, const void* W, const
   return hipGetLastError();
 }
 
-hipError_t launch_flce_chunk(const Layout& L, const void* X, const void* W, const int64_t* y, int64_t ign, int64_t c0,
-                             int64_t rows, char* ws, float* rowloss, void* dX, float* dW, bool first, hipStream_t s) {
+hipError_t launch_flce_chunk(const Layout& L, const void* X, const void* W, const int64_t* y, const float* scale,
+                             int64_t ign, int64_t c0, int64_t rows, char* ws, float* rowloss, void* dX, float* dW,
+                             bool first, hipStream_t s) {
   if (L.dtype == 1)
-    return chunk_impl<__bf16>(L, static_cast<const __bf16*>(X), static_cast<const __bf16*>(W), y, ign, c0, rows, ws,
-                              rowloss, static_cast<__bf16*>(dX), dW, first, s);
-  return chunk_impl<float>(L, static_cast<const float*>(X), static_cast<const float*>(W), y, ign, c0, rows, ws,
+    return chunk_impl<__bf16>(L, static_cast<const __bf16*>(X), static_cast<const __bf16*>(W), y, scale, ign, c0, rows,
+                              ws, rowloss, static_cast<__bf16*>(dX), dW, first, s);
+  return chunk_impl<float>(L, static_cast<const float*>(X), static_cast<const float*>(W), y, scale, ign, c0, rows, ws,
                            rowloss, static_cast<float*>(dX), dW, first, s);
 }
 

@@ -65,12 +65,12 @@ def test_workspace_bound_by_one_chunk(lib):
 
 
 def _call(lib, **kw):
-    a = dict(X=16, W=16, t=16, BT=8, H=128, V=256, ign=-100, C=0, dt=F32, loss=16, rl=None, dX=16, dW=16,
+    a = dict(X=16, W=16, t=16, s=None, BT=8, H=128, V=256, ign=-100, C=0, dt=F32, loss=16, rl=None, dX=16, dW=16,
              ws=256, wsb=1 << 20, err=16, stream=None)
     a.update(kw)
     vp = ctypes.c_void_p
-    return lib.flce_fwd_bwd(vp(a["X"]), vp(a["W"]), vp(a["t"]), a["BT"], a["H"], a["V"], a["ign"], a["C"], a["dt"],
-                            vp(a["loss"]), vp(a["rl"]), vp(a["dX"]), vp(a["dW"]), vp(a["ws"]), a["wsb"],
+    return lib.flce_fwd_bwd(vp(a["X"]), vp(a["W"]), vp(a["t"]), vp(a["s"]), a["BT"], a["H"], a["V"], a["ign"], a["C"],
+                            a["dt"], vp(a["loss"]), vp(a["rl"]), vp(a["dX"]), vp(a["dW"]), vp(a["ws"]), a["wsb"],
                             vp(a["err"]), vp(a["stream"]))
 
 
@@ -95,6 +95,7 @@ def _call(lib, **kw):
         (dict(W=8), 8),
         (dict(ws=128), 8),
         (dict(t=20), 8),
+        (dict(s=18), 8),
         (dict(wsb=16), 3),
     ],
 )
