@@ -9,3 +9,4 @@ from .flce_oracle import (  # noqa: F401
     row_lse,
     valid_rows,
 )
+from .orpo_oracle import orpo_loss_only, orpo_ref, orpo_terms  # noqa: F401,E402

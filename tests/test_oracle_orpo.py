@@ -1,0 +1,84 @@
+"""The ORPO oracle against closed forms and finite differences (CPU only)."""
+import math
+
+import numpy as np
+
+from oracle.orpo_oracle import orpo_loss_only, orpo_ref
+import oracle
+
+IGN = -100
+
+
+def test_two_class_closed_form():
+    """V = 2, one token per sequence, logits (0, c): P = sigmoid(c), so the
+    sequence log odds are exactly c and r = c_w - c_l."""
+    c = np.array([1.3, -0.4, 0.2, 2.0, 0.7, -1.1])  # B = 3 pairs: chosen 0..2, rejected 3..5
+    X = np.stack([c, np.zeros_like(c)], axis=1)     # x_i = (c_i, 0)
+    W = np.array([[0.0, 0.0], [1.0, 0.0]])          # logits (0, c_i)
+    y = np.ones(6, dtype=np.int64)
+    beta = 0.25
+    out = orpo_ref(X, W, y, n_seq=6, beta=beta)
+    sp = lambda x: math.log1p(math.exp(-abs(x))) + max(x, 0.0)  # noqa: E731
+    nll = sum(sp(-c[p]) for p in range(3)) / 3                 # -log sigmoid(c) = softplus(-c)
+    orr = sum(sp(-(c[p] - c[3 + p])) for p in range(3)) / 3
+    expect = nll + beta * orr
+    assert abs(out["loss"] - expect) <= 1e-14 * expect, (out["loss"], expect)
+    assert np.allclose(out["seq_logp"], [-sp(-v) for v in c], rtol=1e-14, atol=0)
+
+
+def _case(seed, n_seq=4, T=3, H=4, V=6, n_ignore=2):
+    r = np.random.default_rng(seed)
+    X = r.standard_normal((n_seq * T, H))
+    W = r.standard_normal((V, H)) * 0.5
+    y = r.integers(0, V, n_seq * T)
+    y[r.choice(n_seq * T, n_ignore, replace=False)] = IGN
+    return X, W, y
+
+
+def test_beta_zero_is_chosen_cross_entropy():
+    X, W, y = _case(61)
+    out = orpo_ref(X, W, y, n_seq=4, beta=0.0)
+    half = X.shape[0] // 2
+    ref = oracle.flce_ref(X[:half], W, y[:half], IGN)
+    assert abs(out["loss"] - ref["loss"]) <= 1e-14 * ref["loss"]
+    assert np.max(np.abs(out["dW"] - ref["dW"])) <= 1e-14 * np.max(np.abs(ref["dW"]))
+    assert np.max(np.abs(out["dX"][:half] - ref["dX"])) <= 1e-14 * np.max(np.abs(ref["dX"]))
+    assert np.all(out["dX"][half:] == 0.0)
+
+
+def test_identical_halves_give_log_two():
+    """Chosen == rejected: every log odds ratio is 0, the odds-ratio term is
+    beta log 2, and its dW contributions cancel between the two halves."""
+    Xh, W, yh = _case(62, n_seq=2, T=4)
+    X = np.concatenate([Xh, Xh])
+    y = np.concatenate([yh, yh])
+    beta = 0.3
+    out = orpo_ref(X, W, y, n_seq=4, beta=beta)
+    ref = oracle.flce_ref(Xh, W, yh, IGN)
+    assert abs(out["loss"] - (ref["loss"] + beta * math.log(2))) <= 1e-13
+    assert np.max(np.abs(out["dW"] - ref["dW"])) <= 1e-13 * np.max(np.abs(ref["dW"]))
+
+
+def test_finite_differences():
+    """dX and dW are the central differences of the loss (written from the
+    logits directly, not through the gradient code), including a pair whose
+    rejected sequence has no valid token."""
+    X, W, y = _case(63, n_seq=6, T=3, H=3, V=5, n_ignore=1)
+    y[5 * 3:6 * 3] = IGN  # sequence 5 (rejected of pair 2) fully ignored
+    beta = 0.7
+    out = orpo_ref(X, W, y, n_seq=6, beta=beta)
+    assert abs(out["loss"] - orpo_loss_only(X, W, y, 6, beta)) <= 1e-14 * out["loss"]
+    h = 1e-6
+    for name, A in (("dX", X), ("dW", W)):
+        num = np.zeros_like(A)
+        for i in range(A.shape[0]):
+            for j in range(A.shape[1]):
+                P, M = A.copy(), A.copy()
+                P[i, j] += h
+                M[i, j] -= h
+                if name == "dX":
+                    num[i, j] = (orpo_loss_only(P, W, y, 6, beta) - orpo_loss_only(M, W, y, 6, beta)) / (2 * h)
+                else:
+                    num[i, j] = (orpo_loss_only(X, P, y, 6, beta) - orpo_loss_only(X, M, y, 6, beta)) / (2 * h)
+        err = float(np.max(np.abs(out[name] - num))) / float(np.max(np.abs(num)))
+        assert err <= 1e-7, (name, err)
