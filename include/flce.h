@@ -116,6 +116,35 @@ int flce_fwd(const void* X, const void* W, const int64_t* targets, int64_t BT, i
              int64_t ignore_index, int64_t chunk_tokens, int dtype, float* loss, float* row_loss, void* workspace,
              size_t workspace_bytes, int32_t* err_flag, void* stream);
 
+/* Bytes of device workspace flce_orpo needs: the larger of the forward-only
+ * and the forward+backward workspaces for n_seq * seq_len tokens, plus three
+ * floats per token and three doubles per sequence.  0 for invalid args. */
+size_t flce_orpo_workspace_bytes(int64_t n_seq, int64_t seq_len, int64_t H, int64_t V, int64_t chunk_tokens,
+                                 int dtype);
+
+/* Fused-linear ORPO (odds-ratio preference) loss and its gradients.  The
+ * pages name the loss (LigerFusedLinearORPOLoss, "Liger-Kernel 項目詳細介紹",
+ * 主要功能) and show the call orpo_loss(lm_head.weight, x, target) (使用方法,
+ * item 4); the objective is the published ORPO one:
+ *   X [n_seq * seq_len, H]: n_seq = 2B sequences, sequence-major; sequences
+ *   0..B-1 are the chosen responses, B..2B-1 the rejected ones (pair p =
+ *   (p, B + p)); targets [n_seq * seq_len] with ignore_index.
+ *   a_s  = mean over the sequence's valid tokens of log softmax(x_i W^T)[y_i]
+ *   r_p  = (a_w - a_l) - (log(1 - e^{a_w}) - log(1 - e^{a_l}))
+ *   loss = mean cross-entropy over the chosen sequences' valid tokens
+ *          + beta / B * sum_p softplus(-r_p)
+ * A pair with a sequence without valid tokens adds nothing to the second
+ * term.  Runs the forward-only pass (token losses), one small kernel for the
+ * sequence terms and the per-token gradient factors, then the fused
+ * forward+backward pass with those factors as token_scale.
+ *   seq_logp [n_seq] float or NULL: a_s (0 for a sequence without valid tokens)
+ *   dX [n_seq * seq_len, H] dtype, dW [V, H] float: d loss / d X, d loss / d W
+ * Other arguments as for flce_fwd_bwd; n_seq must be even and >= 2. */
+int flce_orpo(const void* X, const void* W, const int64_t* targets, int64_t n_seq, int64_t seq_len, int64_t H,
+              int64_t V, int64_t ignore_index, float beta, int64_t chunk_tokens, int dtype, float* loss,
+              float* seq_logp, void* dX, float* dW, void* workspace, size_t workspace_bytes, int32_t* err_flag,
+              void* stream);
+
 /* Bytes of device workspace ce_fwd_bwd_inplace needs (a counter, and BT
  * floats of per-token loss when row_loss is NULL). */
 size_t ce_workspace_bytes(int64_t BT, int64_t V);
@@ -139,8 +168,9 @@ int ce_fwd_bwd_inplace(float* logits, const int64_t* targets, int64_t BT, int64_
  * each kernel kind p < n, the summed duration in ms and the number of timed
  * launches.  Kinds: 0 target count, 1 logits GEMM + softmax statistics,
  * 2 log-sum-exp, 3 in-place logits gradient, 4 dX GEMM, 5 dX split sum,
- * 6 dW GEMM, 7 final mean, 8 logits-only cross-entropy rows, 9 zero fill. */
-#define FLCE_NUM_KERNEL_KINDS 10
+ * 6 dW GEMM, 7 final mean, 8 logits-only cross-entropy rows, 9 zero fill,
+ * 10 ORPO sequence statistics. */
+#define FLCE_NUM_KERNEL_KINDS 11
 int flce_profile_begin(int max_launches);
 int flce_profile_end(double* total_ms, int64_t* launches, int n);
 

@@ -60,6 +60,11 @@ def _declare(lib):
     lib.flce_fwd_workspace_bytes.restype = sz
     lib.flce_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, c.c_int, vp, vp, vp, sz, vp, vp]
     lib.flce_fwd.restype = c.c_int
+    lib.flce_orpo_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, c.c_int]
+    lib.flce_orpo_workspace_bytes.restype = sz
+    lib.flce_orpo.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, c.c_float, i64, c.c_int, vp, vp, vp, vp, vp, sz,
+                              vp, vp]
+    lib.flce_orpo.restype = c.c_int
     lib.ce_workspace_bytes.argtypes = [i64, i64]
     lib.ce_workspace_bytes.restype = sz
     lib.ce_fwd_bwd_inplace.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, sz, vp, vp]
@@ -223,6 +228,45 @@ def flce_forward(X, W, targets, ignore_index: int = -100, chunk_tokens: int = 0,
     return (loss, rl) if row_loss else loss
 
 
+def flce_orpo_workspace_bytes(n_seq: int, seq_len: int, H: int, V: int, chunk_tokens: int = 0,
+                              dtype=torch.bfloat16) -> int:
+    return int(load_library().flce_orpo_workspace_bytes(n_seq, seq_len, H, V, chunk_tokens, _DTYPES[dtype]))
+
+
+def flce_orpo(X, W, targets, beta: float = 0.1, ignore_index: int = -100, chunk_tokens: int = 0, *,
+              seq_logp: bool = False, check: bool = True):
+    """Fused-linear ORPO loss: X [2B, T, H] (or [2B*T, H] with targets
+    [2B, T]), chosen sequences first, W [V, H], targets [2B, T] int64.
+    Returns (loss fp32 0-d, dX shaped like X, dW [V, H] fp32) and, with
+    ``seq_logp=True``, the mean log-probability of each sequence [2B]."""
+    lib = load_library()
+    _check_tensor("W", W, ndim=2)
+    _check_tensor("targets", targets, dtype=torch.int64, ndim=2)
+    _check_tensor("X", X, dtype=W.dtype)
+    if X.dtype not in _DTYPES:
+        raise TypeError(f"dtype {X.dtype} not supported (float32, bfloat16)")
+    n_seq, T = targets.shape
+    V, H = W.shape
+    if X.numel() != n_seq * T * H or X.shape[-1] != H:
+        raise ValueError(f"X{tuple(X.shape)} does not match targets{tuple(targets.shape)} and H={H}")
+    dev = X.device
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    dX = torch.empty_like(X)
+    dW = torch.empty((V, H), dtype=torch.float32, device=dev)
+    err = torch.empty((1,), dtype=torch.int32, device=dev)
+    sl = torch.empty((n_seq,), dtype=torch.float32, device=dev) if seq_logp else None
+    ws = torch.empty((lib.flce_orpo_workspace_bytes(n_seq, T, H, V, chunk_tokens, _DTYPES[X.dtype]),),
+                     dtype=torch.uint8, device=dev)
+    st = lib.flce_orpo(_ptr(X), _ptr(W), _ptr(targets), n_seq, T, H, V, ignore_index, float(beta), chunk_tokens,
+                       _DTYPES[X.dtype], _ptr(loss), _ptr(sl), _ptr(dX), _ptr(dW), _ptr(ws), ws.numel(), _ptr(err),
+                       _stream(dev))
+    if st != 0:
+        raise FlceError(st, "flce_orpo")
+    if check:
+        check_err_flag(err, "flce_orpo")
+    return (loss, dX, dW, sl) if seq_logp else (loss, dX, dW)
+
+
 def ce_fwd_bwd_inplace(logits, targets, ignore_index: int = -100, *, row_loss: bool = False, check: bool = True):
     """Cross-entropy on fp32 logits [BT, V]; overwrites logits with d loss / d logits.
 
@@ -248,7 +292,7 @@ def ce_fwd_bwd_inplace(logits, targets, ignore_index: int = -100, *, row_loss: b
 
 
 KERNEL_KINDS = ["count_valid", "logits", "lse", "grad_inplace", "dx", "dx_reduce", "dw", "loss_final",
-                "ce_rows", "fill_zero"]
+                "ce_rows", "fill_zero", "orpo_stats"]
 
 
 class KernelTimer:
@@ -329,6 +373,44 @@ class _FLCETokenFunction(torch.autograd.Function):
         gx = dX if ctx.needs_input_grad[1] else None
         gw = dW.to(weight.dtype) if ctx.needs_input_grad[0] else None
         return gw, gx, None, None, None
+
+
+class _ORPOFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, weight, x, target, beta, ignore_index, chunk_tokens):
+        loss, dX, dW = flce_orpo(x.contiguous(), weight.contiguous(), target.contiguous(), beta, ignore_index,
+                                 chunk_tokens)
+        ctx.save_for_backward(dX, dW)
+        ctx.weight_dtype = weight.dtype
+        return loss
+
+    @staticmethod
+    def backward(ctx, grad):
+        dX, dW = ctx.saved_tensors
+        if bool(torch.equal(grad, torch.ones_like(grad))):
+            gx = dX if ctx.needs_input_grad[1] else None
+            gw = dW.to(ctx.weight_dtype) if ctx.needs_input_grad[0] else None
+        else:
+            g = grad.to(torch.float32)
+            gx = (dX.float() * g).to(dX.dtype) if ctx.needs_input_grad[1] else None
+            gw = (dW * g).to(ctx.weight_dtype) if ctx.needs_input_grad[0] else None
+        return gw, gx, None, None, None, None
+
+
+class FusedLinearORPOLoss(torch.nn.Module):
+    """``loss = FusedLinearORPOLoss()(lm_head.weight, x, target)`` (the call
+    shape of "Liger-Kernel 項目詳細介紹", 使用方法 item 4): x [2B, T, H] hidden
+    states with the B chosen responses first, target [2B, T]; odds-ratio
+    preference loss with weight ``beta`` plus the chosen-token cross-entropy."""
+
+    def __init__(self, ignore_index: int = -100, beta: float = 0.1, chunk_tokens: int = 0):
+        super().__init__()
+        self.ignore_index = ignore_index
+        self.beta = beta
+        self.chunk_tokens = chunk_tokens
+
+    def forward(self, weight, x, target):
+        return _ORPOFunction.apply(weight, x, target, self.beta, self.ignore_index, self.chunk_tokens)
 
 
 class FusedLinearCrossEntropyLoss(torch.nn.Module):

@@ -22,7 +22,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libflce.so")
-SOURCES = ["api.hip", "kernels_flce.hip", "kernels_ce.hip", "profile.hip"]
+SOURCES = ["api.hip", "kernels_flce.hip", "kernels_ce.hip", "kernels_orpo.hip", "profile.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -142,6 +142,87 @@ int flce_fwd(const void* X, const void* W, const int64_t* targets, int64_t BT, i
   return FLCE_OK;
 }
 
+namespace {
+struct OrpoLayout {
+  size_t off_nvalid, off_rowloss, off_scale, off_scratch, off_region, total;
+  flce::Layout fwd, fb;
+};
+size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+OrpoLayout orpo_layout(int64_t n_seq, int64_t seq_len, int64_t H, int64_t V, int64_t chunk_tokens, int dtype) {
+  OrpoLayout L{};
+  const int64_t BT = n_seq * seq_len;
+  L.fwd = flce::make_fwd_layout(BT, H, V, chunk_tokens, dtype);
+  L.fb = flce::make_layout(BT, H, V, chunk_tokens, dtype);
+  size_t o = 0;
+  L.off_nvalid = o;
+  o = a256(o + 16);
+  L.off_rowloss = o;
+  o = a256(o + (size_t)BT * 4);
+  L.off_scale = o;
+  o = a256(o + (size_t)BT * 4);
+  L.off_scratch = o;
+  o = a256(o + (size_t)n_seq * 3 * 8);
+  L.off_region = o;
+  L.total = o + (L.fwd.total > L.fb.total ? L.fwd.total : L.fb.total);
+  return L;
+}
+}  // namespace
+
+size_t flce_orpo_workspace_bytes(int64_t n_seq, int64_t seq_len, int64_t H, int64_t V, int64_t chunk_tokens,
+                                 int dtype) {
+  if (n_seq < 2 || n_seq % 2 || seq_len <= 0 || H <= 0 || V <= 0 || (dtype != FLCE_F32 && dtype != FLCE_BF16))
+    return 0;
+  return orpo_layout(n_seq, seq_len, H, V, chunk_tokens, dtype).total;
+}
+
+int flce_orpo(const void* X, const void* W, const int64_t* targets, int64_t n_seq, int64_t seq_len, int64_t H,
+              int64_t V, int64_t ignore_index, float beta, int64_t chunk_tokens, int dtype, float* loss,
+              float* seq_logp, void* dX, float* dW, void* workspace, size_t workspace_bytes, int32_t* err_flag,
+              void* stream) {
+  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_ERR_DTYPE;
+  if (n_seq < 2 || n_seq % 2 || seq_len <= 0 || H <= 0 || V <= 0 || V > INT32_MAX || n_seq > INT32_MAX ||
+      seq_len > INT32_MAX / n_seq)
+    return FLCE_ERR_ARG;
+  if (!X || !W || !targets || !loss || !dX || !dW || !workspace || !err_flag) return FLCE_ERR_ARG;
+  if (H % (dtype == FLCE_BF16 ? 8 : 4) != 0) return FLCE_ERR_SHAPE;
+  if (!aligned(W, 16) || !aligned(X, 16) || !aligned(targets, 8) || !aligned(workspace, 256) || !aligned(dW, 4) ||
+      !aligned(dX, dtype == FLCE_BF16 ? 2 : 4) || (seq_logp && !aligned(seq_logp, 4)))
+    return FLCE_ERR_ALIGN;
+  const int64_t BT = n_seq * seq_len;
+  const OrpoLayout L = orpo_layout(n_seq, seq_len, H, V, chunk_tokens, dtype);
+  if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE;
+  if (current_device_ok() != 1) return FLCE_ERR_DEVICE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* nvalid = reinterpret_cast<int32_t*>(ws + L.off_nvalid);
+  float* rl = reinterpret_cast<float*>(ws + L.off_rowloss);
+  float* scale = reinterpret_cast<float*>(ws + L.off_scale);
+  double* scratch = reinterpret_cast<double*>(ws + L.off_scratch);
+  char* region = ws + L.off_region;
+
+  if (flce::launch_count_valid(targets, BT, V, ignore_index, nvalid, err_flag, s) != hipSuccess)
+    return FLCE_ERR_LAUNCH;
+  // token losses (forward only)
+  for (int64_t c0 = 0; c0 < BT; c0 += L.fwd.C) {
+    const int64_t rows = BT - c0 < L.fwd.C ? BT - c0 : L.fwd.C;
+    if (flce::launch_fwd_chunk(L.fwd, X, W, targets, ignore_index, c0, rows, region, rl, s) != hipSuccess)
+      return FLCE_ERR_LAUNCH;
+  }
+  // sequence terms, loss, per-token gradient factors
+  if (flce::launch_orpo_stats(rl, targets, n_seq, seq_len, ignore_index, beta, scale, seq_logp, loss, scratch, s) !=
+      hipSuccess)
+    return FLCE_ERR_LAUNCH;
+  // gradients: the fused pass with those factors (its token losses repeat the ones above)
+  for (int64_t c0 = 0; c0 < BT; c0 += L.fb.C) {
+    const int64_t rows = BT - c0 < L.fb.C ? BT - c0 : L.fb.C;
+    if (flce::launch_flce_chunk(L.fb, X, W, targets, scale, ignore_index, c0, rows, region, rl, dX, dW, c0 == 0,
+                                s) != hipSuccess)
+      return FLCE_ERR_LAUNCH;
+  }
+  return FLCE_OK;
+}
+
 size_t ce_workspace_bytes(int64_t BT, int64_t V) {
   if (BT < 0 || V <= 0) return 0;
   return 256 + (((size_t)(BT > 0 ? BT : 1) * 4 + 255) & ~(size_t)255);

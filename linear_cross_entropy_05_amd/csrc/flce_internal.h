@@ -38,6 +38,7 @@ enum Phase {
   kPhaseLoss,       // final mean
   kPhaseCeRows,     // logits-only cross-entropy rows
   kPhaseFill,       // zero fill
+  kPhaseOrpo,       // ORPO sequence statistics and token gradient factors
   kNumPhases
 };
 
@@ -63,6 +64,8 @@ hipError_t launch_flce_chunk(const Layout& L, const void* X, const void* W, cons
 hipError_t launch_fwd_chunk(const Layout& L, const void* X, const void* W, const int64_t* y, int64_t ignore_index,
                             int64_t c0, int64_t rows, char* ws, float* rowloss, hipStream_t s);
 hipError_t launch_loss_final(const float* rowloss, int64_t BT, const int32_t* nvalid, float* loss, hipStream_t s);
+hipError_t launch_orpo_stats(const float* rowloss, const int64_t* y, int64_t n_seq, int64_t T, int64_t ign, float beta,
+                             float* scale, float* seq_logp, float* loss, double* scratch, hipStream_t s);
 hipError_t launch_ce_rows(float* logits, const int64_t* y, int64_t BT, int64_t V, int64_t ignore_index,
                           const int32_t* nvalid, float* rowloss, hipStream_t s);
 

@@ -22,11 +22,11 @@ ProfScope::ProfScope(int phase, hipStream_t s) : idx_(-1), s_(s) {
   if (!g_prof.on || 2 * g_prof.next + 1 >= g_prof.ev.size()) return;
   idx_ = (long)g_prof.next++;
   g_prof.phase[idx_] = phase;
-  hipEventRecord(g_prof.ev[2 * idx_], s_);
+  (void)hipEventRecord(g_prof.ev[2 * idx_], s_);
 }
 
 ProfScope::~ProfScope() {
-  if (idx_ >= 0) hipEventRecord(g_prof.ev[2 * idx_ + 1], s_);
+  if (idx_ >= 0) (void)hipEventRecord(g_prof.ev[2 * idx_ + 1], s_);
 }
 
 }  // namespace flce
@@ -67,7 +67,7 @@ int flce_profile_end(double* total_ms, int64_t* launches, int n) {
       if (launches) launches[p] += 1;
     }
   }
-  for (auto e : g_prof.ev) hipEventDestroy(e);
+  for (auto e : g_prof.ev) (void)hipEventDestroy(e);
   g_prof.ev.clear();
   g_prof.phase.clear();
   g_prof.next = 0;

@@ -23,6 +23,8 @@ def test_exports_every_declared_function(lib):
         "flce_fwd_bwd",
         "flce_fwd",
         "flce_fwd_workspace_bytes",
+        "flce_orpo",
+        "flce_orpo_workspace_bytes",
         "ce_fwd_bwd_inplace",
         "flce_workspace_bytes",
         "ce_workspace_bytes",
@@ -171,3 +173,43 @@ def test_no_cpu_fallback_in_product_code():
         text = p.read_text(errors="ignore")
         assert "oracle" not in text.lower().replace("oracle-free", ""), p
         assert "synth_inputs" not in text, p
+
+
+def _call_orpo(lib, **kw):
+    a = dict(X=16, W=16, t=16, ns=4, T=8, H=128, V=256, ign=-100, beta=0.1, C=0, dt=F32, loss=16, sl=None, dX=16,
+             dW=16, ws=256, wsb=1 << 24, err=16, stream=None)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return lib.flce_orpo(vp(a["X"]), vp(a["W"]), vp(a["t"]), a["ns"], a["T"], a["H"], a["V"], a["ign"],
+                         ctypes.c_float(a["beta"]), a["C"], a["dt"], vp(a["loss"]), vp(a["sl"]), vp(a["dX"]),
+                         vp(a["dW"]), vp(a["ws"]), a["wsb"], vp(a["err"]), vp(a["stream"]))
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(dt=3), 2),
+        (dict(ns=3), 1),
+        (dict(ns=0), 1),
+        (dict(T=0), 1),
+        (dict(H=0), 1),
+        (dict(X=None), 1),
+        (dict(dX=None), 1),
+        (dict(H=130), 7),
+        (dict(X=24), 8),
+        (dict(sl=18), 8),
+        (dict(ws=128), 8),
+        (dict(wsb=16), 3),
+    ],
+)
+def test_orpo_host_argument_checks(lib, kw, status):
+    assert _call_orpo(lib, **kw) == status
+
+
+def test_orpo_workspace(lib):
+    # the larger of the two passes' workspaces plus per-token and per-sequence arrays
+    ws = lib.flce_orpo_workspace_bytes(8, 1024, 4096, 128256, 0, BF16)
+    fb = lib.flce_workspace_bytes(8192, 4096, 128256, 0, BF16)
+    assert fb < ws <= fb + 8192 * 8 + 8 * 24 + 4096
+    assert lib.flce_orpo_workspace_bytes(3, 1024, 4096, 128256, 0, BF16) == 0
+    assert lib.flce_orpo_workspace_bytes(8, 0, 4096, 128256, 0, BF16) == 0

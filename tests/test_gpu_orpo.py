@@ -1,0 +1,93 @@
+"""Fused-linear ORPO (flce_orpo) on the GPU against the float64 ORPO oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+from gpu_helpers import TOL, ensure_built, rel_err, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return ensure_built()
+
+
+def _inputs(n_seq, T, H, V, dtype, seed, ignore_seq=None, w_std=0.05):
+    w = si.small(n_seq * T, H, V, dtype, seed=seed, w_std=w_std)
+    X, W, y = si.make_inputs(w)
+    y = y.clone()
+    if ignore_seq is not None:
+        y[ignore_seq * T:(ignore_seq + 1) * T] = w.ignore_index
+    return w, X, W, y
+
+
+def _run(n_seq, T, H, V, dtype, seed, beta=0.1, chunk=0, ignore_seq=None):
+    import linear_cross_entropy_05_amd as flce
+
+    w, X, W, y = _inputs(n_seq, T, H, V, dtype, seed, ignore_seq)
+    dev = torch.device("cuda", 0)
+    say(f"[gpu] flce_orpo n_seq={n_seq} T={T} H={H} V={V} {dtype} beta={beta} chunk={chunk}")
+    loss, dX, dW, sl = flce.flce_orpo(X.to(dev), W.to(dev), y.to(dev).view(n_seq, T), beta, w.ignore_index, chunk,
+                                      seq_logp=True)
+    torch.cuda.synchronize()
+    ref = oracle.orpo_ref(X, W, y, n_seq, beta, w.ignore_index)
+    tl, tg = TOL[dtype]
+    el = abs(loss.item() - ref["loss"]) / abs(ref["loss"])
+    es = rel_err(to_np(sl), ref["seq_logp"])
+    ex, ew = rel_err(to_np(dX), ref["dX"]), rel_err(to_np(dW), ref["dW"])
+    say(f"  loss {loss.item():.7f} ref {ref['loss']:.7f} err {el:.2e}; seq logp {es:.2e}; dX {ex:.2e}; dW {ew:.2e}")
+    assert el <= tl and es <= tl and ex <= tg and ew <= tg
+    return (X, W, y), (loss, dX, dW, sl), ref
+
+
+def test_orpo_fp32_ragged():
+    _run(4, 37, 64, 300, "fp32", seed=71)
+
+
+def test_orpo_bf16_multi_tile():
+    _run(6, 130, 200, 1000, "bf16", seed=72, beta=0.2)
+
+
+def test_orpo_bf16_chunked_with_empty_sequence():
+    # rejected sequence of pair 1 has no valid token; several token chunks
+    _run(4, 160, 136, 700, "bf16", seed=73, beta=0.5, chunk=200, ignore_seq=3)
+
+
+def test_orpo_beta_zero_is_chosen_cross_entropy():
+    import linear_cross_entropy_05_amd as flce
+
+    n_seq, T, H, V = 4, 64, 128, 500
+    w, X, W, y = _inputs(n_seq, T, H, V, "fp32", seed=74)
+    dev = torch.device("cuda", 0)
+    loss, dX, dW = flce.flce_orpo(X.to(dev), W.to(dev), y.to(dev).view(n_seq, T), 0.0, w.ignore_index)
+    half = n_seq * T // 2
+    l2, dX2, dW2 = flce.flce_fwd_bwd(X[:half].to(dev), W.to(dev), y[:half].to(dev), w.ignore_index)
+    torch.cuda.synchronize()
+    assert abs(loss.item() - l2.item()) <= 1e-6 * abs(l2.item())
+    assert torch.equal(dX[:half], dX2) and float(dX[half:].abs().max()) == 0.0
+    assert rel_err(to_np(dW), to_np(dW2)) <= 1e-6
+
+
+def test_orpo_module_autograd():
+    import linear_cross_entropy_05_amd as flce
+
+    n_seq, T, H, V = 4, 50, 96, 400
+    w, X, W, y = _inputs(n_seq, T, H, V, "bf16", seed=75)
+    dev = torch.device("cuda", 0)
+    Wg = W.to(dev).requires_grad_(True)
+    Xg = X.to(dev).view(n_seq, T, H).clone().requires_grad_(True)
+    mod = flce.FusedLinearORPOLoss(ignore_index=w.ignore_index, beta=0.1)
+    loss = mod(Wg, Xg, y.to(dev).view(n_seq, T))
+    (2.0 * loss).backward()
+    torch.cuda.synchronize()
+    ref = oracle.orpo_ref(X, W, y, n_seq, 0.1, w.ignore_index)
+    tl, tg = TOL["bf16"]
+    assert abs(loss.item() - ref["loss"]) / ref["loss"] <= tl
+    assert Xg.grad.shape == (n_seq, T, H) and Wg.grad.dtype == torch.bfloat16
+    assert rel_err(to_np(Xg.grad).reshape(-1, H), 2.0 * ref["dX"]) <= tg
+    assert rel_err(to_np(Wg.grad), 2.0 * ref["dW"]) <= tg
