@@ -88,9 +88,10 @@ def gpu_bench(w, steps, warmup, forward=True):
     wall_ms = (wall1 - wall0) * 1e3 / steps
 
     # forward only (evaluation path), timed separately and reported as context
-    fwd_ms = None
+    fwd_ms = orpo = None
     if forward:
         fwd_ms = time_forward(flce, w, Xd, Wd, yd, steps, stream, float(out[0].item()))
+        orpo = time_orpo(flce, w, Xd, Wd, yd, stream)
     err = int(out[3].item())
     if err != 0:
         raise RuntimeError(f"device reported error flag {err}")
@@ -100,7 +101,8 @@ def gpu_bench(w, steps, warmup, forward=True):
                for k in kt.ms if kt.launches[k]}
     log(f"[bench] {ms:.3f} ms/step (wall {wall_ms:.3f}); kernels: "
         + ", ".join(f"{k} {v['ms_per_step']:.3f}" for k, v in kernels.items()))
-    return {"ms": ms, "fwd_ms": fwd_ms, "C": C, "ws_bytes": ws_bytes, "peak_extra": peak_extra, "loss": loss,
+    return {"ms": ms, "fwd_ms": fwd_ms, "orpo": orpo, "C": C, "ws_bytes": ws_bytes, "peak_extra": peak_extra,
+            "loss": loss,
             "kernels": kernels,
             "cus": props.multi_processor_count, "arch": getattr(props, "gcnArchName", "?")}
 
@@ -129,6 +131,30 @@ def time_forward(flce, w, Xd, Wd, yd, steps, stream, loss_fwd_bwd):
         raise RuntimeError("forward-only loss differs from the fwd+bwd loss")
     log(f"[bench] forward only: {fwd_ms:.3f} ms/step")
     return fwd_ms
+
+
+def time_orpo(flce, w, Xd, Wd, yd, stream, seq_len=1024, reps=3):
+    """Fused-linear ORPO on the same tokens read as BT / seq_len sequences
+    (first half chosen, second half rejected): ms per call (context)."""
+    import torch
+
+    n_seq = w.BT // seq_len
+    if n_seq < 2 or n_seq % 2 or n_seq * seq_len != w.BT:
+        return None
+    y2 = yd.view(n_seq, seq_len)
+    flce.flce_orpo(Xd, Wd, y2, 0.1, w.ignore_index)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        flce.flce_orpo(Xd, Wd, y2, 0.1, w.ignore_index, check=False)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    log(f"[bench] ORPO ({n_seq} sequences of {seq_len}): {ms:.3f} ms/call")
+    return {"ms_per_call": round(ms, 4), "sequences": n_seq, "seq_len": seq_len, "beta": 0.1,
+            "tokens_per_s": round(w.BT / (ms * 1e-3), 1)}
 
 
 def copy_calibration(nbytes=256 << 20, reps=3):
@@ -266,6 +292,7 @@ def main(argv=None):
         "dominant_kernel": dom,
         "roofline": roof,
         "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in r["kernels"].items()},
+        "orpo": r["orpo"],
         "forward_only": None if r["fwd_ms"] is None else {
             "ms_per_step": round(r["fwd_ms"], 4), "tokens_per_s": round(w.BT / (r["fwd_ms"] * 1e-3), 1),
             "tflops": round(2.0 * w.BT * w.H * w.V / (r["fwd_ms"] * 1e-3) / 1e12, 2)},
