@@ -64,9 +64,10 @@ enum flce_status {
 };
 
 /* Tokens per chunk that flce_fwd_bwd will use: chunk_tokens if positive
- * (capped at BT), else the largest power of two whose logits chunk
- * (chunk x round_up(V, 256) elements of the dtype) fits in 1 GiB, capped at BT.
- * Returns 0 for invalid arguments. */
+ * (capped at BT); otherwise the fewest chunks whose logits buffer
+ * (chunk x round_up(V, 256) elements of the dtype) fits in 1 GiB, made equal
+ * and rounded up to a multiple of 256 tokens (never above the 1 GiB bound),
+ * capped at BT.  Returns 0 for invalid arguments. */
 int64_t flce_chunk_tokens(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);
 
 /* Bytes of device workspace flce_fwd_bwd needs for these sizes: one logits

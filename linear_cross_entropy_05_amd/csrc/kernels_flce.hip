@@ -538,9 +538,18 @@ Layout make_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int d
   L.nvt = (V + kTile - 1) / kTile;
   int64_t C = chunk_tokens;
   if (C <= 0) {
-    // largest power of two whose chunk buffer fits in 1 GiB
-    C = 1;
-    while ((C * 2) * L.ldz * L.esize <= (int64_t(1) << 30)) C *= 2;
+    // as few chunks as keep the chunk buffer within 1 GiB, of equal size
+    // rounded up to whole 256-token tiles (each chunk after the first costs
+    // a read-modify-write of the fp32 dW)
+    const int64_t cmax = ((int64_t)1 << 30) / (L.ldz * L.esize);
+    if (cmax < kTile || BT <= cmax) {
+      C = cmax < 1 ? 1 : cmax;
+    } else {
+      const int64_t nch = (BT + cmax - 1) / cmax;
+      C = ((BT + nch - 1) / nch + kTile - 1) / kTile * kTile;
+      const int64_t cmax_tiles = cmax / kTile * kTile;
+      if (C > cmax_tiles) C = cmax_tiles;
+    }
   }
   if (C > BT) C = BT;
   if (C < 1) C = 1;

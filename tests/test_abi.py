@@ -43,10 +43,12 @@ def test_status_strings(lib):
 
 
 def test_chunk_rule(lib):
-    # largest power of two with a chunk (C x round_up(V, 256) elements) <= 1 GiB, capped at BT
-    assert lib.flce_chunk_tokens(8192, 4096, 128256, 0, BF16) == 4096
-    assert lib.flce_chunk_tokens(16384, 3584, 152064, 0, BF16) == 2048
-    assert lib.flce_chunk_tokens(8192, 3072, 256000, 0, BF16) == 2048
+    # fewest chunks with C x round_up(V, 256) elements <= 1 GiB, equal, rounded up to 256 tokens
+    assert lib.flce_chunk_tokens(8192, 4096, 128256, 0, BF16) == 4096  # 2 chunks
+    assert lib.flce_chunk_tokens(16384, 3584, 152064, 0, BF16) == 3328  # 5 chunks (at most 3530 tokens fit)
+    assert lib.flce_chunk_tokens(8192, 3072, 256000, 0, BF16) == 2048  # 4 chunks
+    assert lib.flce_chunk_tokens(4000, 4096, 128256, 0, BF16) == 4000  # fits whole
+    assert lib.flce_chunk_tokens(5000, 4096, 128256, 0, BF16) == 2560  # 2 chunks of 2500 -> 2560
     assert lib.flce_chunk_tokens(2048, 2048, 32000, 1024, BF16) == 1024
     assert lib.flce_chunk_tokens(8, 128, 256, 8, F32) == 8
     assert lib.flce_chunk_tokens(100, 128, 256, 0, F32) == 100
