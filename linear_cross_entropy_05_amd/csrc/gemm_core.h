@@ -1,31 +1,30 @@
 // MFMA tile GEMM building blocks for gfx950 (CDNA4), shared by the three
 // contractions of fused linear + cross-entropy:
 //   logits   Z^T[v,c] = sum_h W[v,h] X[c,h]     (both operands K-contiguous)
-//   dX       dX[c,h]  = sum_v G[c,v] W[v,h]     (W read K-major: transposed)
-//   dW       dW[v,h] += sum_c G[c,v] X[c,h]     (both read K-major: transposed)
+//   dX       dX[c,h]  = sum_v G[c,v] W[v,h]     (W read K-major)
+//   dW       dW[v,h] += sum_c G[c,v] X[c,h]     (both read K-major)
 //
 // A workgroup of 256 threads (4 wave64s, 2 x 2) owns a 256 x 256 output tile;
 // each wave owns 128 x 128 = 4 x 4 MFMA 32x32 blocks (16 fp32 accumulators
-// per lane per block).  K advances 128 bytes per stage (64 bf16 or 32 fp32),
-// double-buffered in LDS: 2 stages x 2 operands x 32 KiB = 128 KiB of the
-// 160 KiB gfx950 LDS.
+// per lane per block, held in the AGPRs).  K advances 128 bytes per stage
+// (64 bf16 or 32 fp32), double-buffered in LDS: 2 stages x 2 operands x
+// 32 KiB = 128 KiB of the 160 KiB gfx950 LDS.
 //
-// LDS holds every operand "row-major in K": tile row r (an M or N index) is
-// 128 bytes of consecutive K, split into eight 16-byte chunks.  Chunk c of row
-// r sits at slot (c ^ r ^ (r >> 3)) & 7, which keeps both the row-wise MFMA
-// fragment reads and the transposing writes free of bank conflicts.
-//
-// Operands stored K-contiguous in HBM are copied chunk by chunk.  Operands
-// stored K-major (MN contiguous) are loaded as 8 x 8 (bf16) or 4 x 4 (fp32)
-// element blocks, one 16-byte load per K row, transposed in registers and
-// written as K-contiguous chunks.
+// bf16 operands use the direct-to-LDS pipeline of namespace `pipe` below
+// (copies straight from HBM into LDS, transposing LDS reads for K-major
+// operands).  fp32 operands use the register-staged loop that follows here:
+// each stage is loaded into registers (K-contiguous operands chunk by chunk;
+// K-major ones as 4 x 4 blocks transposed in registers) and written to LDS
+// "row-major in K" -- tile row r (an M or N index) is 128 bytes of consecutive
+// K in eight 16-byte chunks, chunk c at slot (c ^ r ^ (r >> 3)) & 7, free of
+// bank conflicts for the row-wise fragment reads and the transposing writes.
 //
 // MFMA operand mapping: for v_mfma_f32_32x32x16_bf16 lane l feeds row
 // (l % 32) of its operand with the 8 K values of chunk (2 s + l / 32) of the
-// current stage (s = 0..3).  A and B use the same K assignment, so the
-// contraction is exact whatever order the hardware sums the K slots in.  The
-// fp32 path issues four v_mfma_f32_32x32x2f32 per chunk pair, element t of
-// each lane's chunk feeding the t-th instruction.  Accumulator element e of
+// current 64-deep stage (s = 0..3).  A and B use the same K assignment, so
+// the contraction is exact whatever order the hardware sums the K slots in.
+// The fp32 path issues four v_mfma_f32_32x32x2f32 per chunk pair, element t
+// of each lane's chunk feeding the t-th instruction.  Accumulator element e of
 // lane l is output row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32.
 #pragma once
 
@@ -181,23 +180,6 @@ __device__ __forceinline__ void store_kcontig(char* lds, const u32x4 (&st)[8], i
 
 template <typename T>
 __device__ __forceinline__ void store_kmajor(char* lds, const u32x4 (&st)[8], int tid);
-
-// 8 x 8 bf16 transpose: st[j] holds K row j, MN columns 0..7 (two per dword).
-// Output row p (MN column p) gets K values 0..7 packed two per dword.
-template <>
-__device__ __forceinline__ void store_kmajor<__bf16>(char* lds, const u32x4 (&st)[8], int tid) {
-  const int mc = tid & 31, kb = tid >> 5;
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    u32x4 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = st[2 * q][p >> 1], hi = st[2 * q + 1][p >> 1];
-      o[q] = (p & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-    *reinterpret_cast<u32x4*>(lds + lds_off(mc * 8 + p, kb)) = o;
-  }
-}
 
 template <>
 __device__ __forceinline__ void store_kmajor<float>(char* lds, const u32x4 (&st)[8], int tid) {
