@@ -7,12 +7,13 @@
 // A workgroup of 256 threads (4 wave64s, 2 x 2) owns a 256 x 256 output tile;
 // each wave owns 128 x 128 = 4 x 4 MFMA 32x32 blocks (16 fp32 accumulators
 // per lane per block, held in the AGPRs).  K advances 128 bytes per stage
-// (64 bf16 or 32 fp32), double-buffered in LDS: 2 stages x 2 operands x
-// 32 KiB = 128 KiB of the 160 KiB gfx950 LDS.
+// (64 bf16 or 32 fp32); one operand's tile of one stage is 32 KiB of LDS.
 //
 // bf16 operands use the direct-to-LDS pipeline of namespace `pipe` below
-// (copies straight from HBM into LDS, transposing LDS reads for K-major
-// operands).  fp32 operands use the register-staged loop that follows here:
+// (copies straight from HBM into a ring of five 32 KiB LDS slabs, all 160 KiB
+// of gfx950 LDS; transposing LDS reads for K-major operands).  fp32 operands
+// use the double-buffered (2 stages x 2 operands, 128 KiB) register-staged
+// loop that follows here:
 // each stage is loaded into registers (K-contiguous operands chunk by chunk;
 // K-major ones as 4 x 4 blocks transposed in registers) and written to LDS
 // "row-major in K" -- tile row r (an M or N index) is 128 bytes of consecutive
@@ -330,7 +331,9 @@ namespace pipe {
 constexpr int kBK = 64;           // bf16 K per stage
 constexpr int kRowB = 128;        // bytes per K-contiguous tile row per stage
 constexpr int kOp = 256 * kRowB;  // 32 KiB per operand per stage
-constexpr int kStage = 2 * kOp;   // 64 KiB
+constexpr int kSlab = kOp;        // LDS ring slot: one operand tile of one stage
+constexpr int kSlabs = 5;
+constexpr int kRingBytes = kSlabs * kSlab;  // 160 KiB, all of the gfx950 LDS
 constexpr int kLoads = 8;         // 1 KiB copies per wave per operand per stage
 
 typedef __attribute__((address_space(3))) void* lds_void;
@@ -377,14 +380,12 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 // 8 w + 32 q .. + 7; lane i fills row 8 w + 32 q + i / 8, slot i % 8.
 struct KcLoader {
   u32x4 r;
-  Rsrc rr;  // the same resource, for the compiler-visible copy below
   uint32_t voff[kLoads];
   uint32_t kch;  // K offset (elements) of this lane's chunk, the same for every copy
   int64_t kend;
   __device__ __forceinline__ void init(const Operand<__bf16>& op, int64_t mn0, int wave, int lane) {
     const int64_t nrows = op.rows - mn0 < kTile ? op.rows - mn0 : kTile;
     r = rsrc_words(op.base + mn0 * op.ld, nrows * op.ld * 2);
-    rr = make_rsrc(op.base + mn0 * op.ld, nrows * op.ld * 2);
     kend = op.cols;
     const uint32_t row = 8 * wave + (lane >> 3);  // < 32: the swizzle is that of every copy's row
     const uint32_t c = ((lane & 7) ^ kc_sw(row)) & 7u;
@@ -392,26 +393,8 @@ struct KcLoader {
 #pragma unroll
     for (int q = 0; q < kLoads; ++q) voff[q] = (uint32_t)(((row + 32 * q) * op.ld + 8 * c) * 2);
   }
-  // tile: LDS byte address of this operand's stage tile
-  __device__ __forceinline__ void issue(uint32_t tile, int64_t k0, int wave) const {
-    const uint32_t soff = (uint32_t)(k0 * 2);
-    const uint32_t dst = tile + 1024 * wave;
-    if (k0 + kBK <= kend) {
-#pragma unroll
-      for (int q = 0; q < kLoads; ++q) dma16(r, dst + 4096 * q, voff[q], soff);
-    } else {
-      // K tail: chunks past the bound read as zero
-      const bool in = k0 + kch < kend;
-#pragma unroll
-      for (int q = 0; q < kLoads; ++q) dma16(r, dst + 4096 * q, in ? voff[q] : 0x80000000u, soff);
-    }
-  }
-  __device__ __forceinline__ u32x4 frag(const char* tile, int row, int c) const {
-    return *reinterpret_cast<const u32x4*>(tile + kc_off(row, c));
-  }
-  // One copy at a time, as the compiler's own LDS-copy intrinsic (so the
-  // scheduler can place it between MFMAs).  `in` false: every lane reads out
-  // of bounds and the copy writes zeros.
+  // the copies of the stage starting at K offset k0; `more` false: every
+  // lane reads out of bounds and the copies write zeros
   struct Stage {
     uint32_t soff;
     bool in;
@@ -419,10 +402,12 @@ struct KcLoader {
   __device__ __forceinline__ Stage stage(int64_t k0, bool more) const {
     return Stage{(uint32_t)(k0 * 2), more && (k0 + kBK <= kend || k0 + kch < kend)};
   }
-  __device__ __forceinline__ void issue_one(const Stage& st, uint32_t tile, int q, int wave) const {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rr, (__attribute__((address_space(3))) void*)(uintptr_t)(tile + 1024 * wave + 4096 * q), 16,
-        st.in ? (int)voff[q] : (int)0x80000000, (int)st.soff, 0, 0);
+  // copy q of this wave into the operand tile at LDS byte address `tile`
+  __device__ __forceinline__ void issue(const Stage& st, uint32_t tile, int q, int wave) const {
+    dma16(r, tile + 1024 * wave + 4096 * q, st.in ? voff[q] : 0x80000000u, st.soff);
+  }
+  __device__ __forceinline__ u32x4 frag(const char* tile, int row, int c) const {
+    return *reinterpret_cast<const u32x4*>(tile + kc_off(row, c));
   }
 };
 
@@ -444,15 +429,19 @@ struct KmLoader {
 #pragma unroll
     for (int q = 0; q < kLoads; ++q) voff[q] = (uint32_t)(((k + 8 * q) * ld + 16 * seg + 8 * (lane & 1)) * 2);
   }
-  __device__ __forceinline__ void issue(uint32_t tile, int64_t k0, int wave) const {
-    // the buffer ends at the last element of the operand: K rows past it and
-    // MN columns past it on the last K row read as zero (MN columns past the
-    // tile edge on earlier rows feed only outputs that are never stored)
-    const int64_t nb = rows > k0 ? ((rows - k0 - 1) * ld + (cols - mn0)) * 2 : 0;
-    const u32x4 r = rsrc_words(base + k0 * ld + mn0, nb);
-    const uint32_t dst = tile + 1024 * wave;
-#pragma unroll
-    for (int q = 0; q < kLoads; ++q) dma16(r, dst + 4096 * q, voff[q], 0);
+  // One resource per stage, starting at K row k0: it ends at the last element
+  // of the operand, so K rows past it and MN columns past it on the last K
+  // row read as zero (MN columns past the tile edge on earlier rows feed only
+  // outputs that are never stored).  `more` false: an empty resource, zeros.
+  struct Stage {
+    u32x4 r;
+  };
+  __device__ __forceinline__ Stage stage(int64_t k0, bool more) const {
+    const int64_t nb = (more && rows > k0) ? ((rows - k0 - 1) * ld + (cols - mn0)) * 2 : 0;
+    return Stage{rsrc_words(base + (more ? k0 * ld + mn0 : 0), nb)};
+  }
+  __device__ __forceinline__ void issue(const Stage& st, uint32_t tile, int q, int wave) const {
+    dma16(st.r, tile + 1024 * wave + 4096 * q, voff[q], 0);
   }
   // fragment of MN columns nb .. nb + 31, K rows 16 s + 8 (lane / 32) .. + 7
   __device__ __forceinline__ u32x4 frag(const char* tile, int nb, int s, int lane) const {
@@ -469,12 +458,18 @@ struct KmLoader {
 template <bool kKMajor>
 using LoaderT = typename std::conditional<kKMajor, KmLoader, KcLoader>::type;
 
+// this wave's four fragments of step s (16 of K) of one operand tile: rows
+// (or columns) w 128 + 32 i .. + 31
 template <bool kKMajor>
-__device__ __forceinline__ u32x4 read_frag(const LoaderT<kKMajor>& l, const char* tile, int rb, int s, int lane) {
-  if constexpr (kKMajor)
-    return l.frag(tile, rb, s, lane);
-  else
-    return l.frag(tile, rb + (lane & 31), 2 * s + (lane >> 5));
+__device__ __forceinline__ void load_frags(const LoaderT<kKMajor>& l, const char* tile, int s, int w, int lane,
+                                           u32x4 (&f)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (kKMajor)
+      f[i] = l.frag(tile, w * 128 + 32 * i, s, lane);
+    else
+      f[i] = l.frag(tile, w * 128 + 32 * i + (lane & 31), 2 * s + (lane >> 5));
+  }
 }
 
 // s_waitcnt vmcnt(N): at most N of this wave's copies still in flight
@@ -484,167 +479,146 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// fragments of step s (16 of K) of a stage: this wave's four A row blocks and
-// four B row blocks
-template <bool kAKMajor, bool kBKMajor>
-__device__ __forceinline__ void load_step(const LoaderT<kAKMajor>& la, const LoaderT<kBKMajor>& lb, const char* tile,
-                                          int s, int wy, int wx, int lane, u32x4 (&fa)[4], u32x4 (&fb)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) fa[i] = read_frag<kAKMajor>(la, tile, wy * 128 + 32 * i, s, lane);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) fb[j] = read_frag<kBKMajor>(lb, tile + kOp, wx * 128 + 32 * j, s, lane);
+// At most N of this wave's copies in flight and its LDS reads done, then the
+// workgroup barrier.  No compiler fence: __syncthreads() would also wait for
+// the copies issued after the ones this barrier is for.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
-__device__ __forceinline__ void mma_step(const u32x4 (&fa)[4], const u32x4 (&fb)[4], f32x16 (&acc)[4][4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = mma_chunk<__bf16>(fa[i], fb[j], acc[i][j]);
-}
+__device__ __forceinline__ uint32_t mod5(uint32_t x) { return x >= 5 ? x - 5 : x; }
 
-// One tile's pass over K, split so that a persistent kernel can start the
-// copies of its next tile (init + prologue) before the epilogue of the
-// current one.  run() expects prologue() to have been issued by this
-// workgroup and ends with a barrier after which the stage buffers are free.
-template <bool kAKMajor, bool kBKMajor>
-struct Pipe {
-  LoaderT<kAKMajor> la;
-  LoaderT<kBKMajor> lb;
-  int64_t k0;
-  int nk;
-
-  __device__ __forceinline__ void init(const Operand<__bf16>& A, int64_t m0, const Operand<__bf16>& B, int64_t n0,
-                                       int64_t k0_, int64_t k1) {
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    k0 = k0_;
-    nk = (int)((k1 - k0 + kBK - 1) / kBK);
-    if (nk < 0) nk = 0;
-    la.init(A, m0, wave, lane);
-    lb.init(B, n0, wave, lane);
-  }
-
-  // copies of stages 0 and 1 into buffers 0 and 1 (no wait)
-  __device__ __forceinline__ void prologue(uint32_t lds0) const {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (nk > 0) {
-      la.issue(lds0, k0, wave);
-      lb.issue(lds0 + kOp, k0, wave);
-    }
-    if (nk > 1) {
-      la.issue(lds0 + kStage, k0 + kBK, wave);
-      lb.issue(lds0 + kStage + kOp, k0 + kBK, wave);
-    }
-  }
-
-  // With both operands K-contiguous the copies of stage k + 2 are issued one
-  // per MFMA of stage k's last step (measured: +10% on the logits product);
-  // with a K-major operand the burst issue is faster, so it stays.
-  static constexpr bool kInterleave = !kAKMajor && !kBKMajor;
-
-  // `pending`: copies this wave issued after the prologue and before run()
-  // (they complete after it, so the first wait leaves them in flight)
-  template <int kPending = 0>
-  __device__ __forceinline__ void run(char* smem, f32x16 (&acc)[4][4]) const {
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wy = wave >> 1, wx = wave & 1;
-    const uint32_t lds0 = lds_addr(smem);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-    if (nk <= 0) {
-      wait_vm<0>();
-      __syncthreads();
-      return;
-    }
-    if (nk > 1)
-      wait_vm<2 * kLoads + kPending>();
-    else
-      wait_vm<kPending>();
-    __syncthreads();
-
-    u32x4 fa[2][4], fb[2][4];
-    load_step<kAKMajor, kBKMajor>(la, lb, smem, 0, wy, wx, lane, fa[0], fb[0]);
-    // every iteration of this loop has a next stage; the last stage follows
-    for (int kt = 0; kt + 1 < nk; ++kt) {
-      const char* cur = smem + (kt & 1) * kStage;
-#pragma unroll
-      for (int s = 0; s < 3; ++s) {
-        load_step<kAKMajor, kBKMajor>(la, lb, cur, s + 1, wy, wx, lane, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-        // keep these reads ahead of the MFMAs below
-        __builtin_amdgcn_sched_barrier(0);
-        mma_step(fa[s & 1], fb[s & 1], acc);
-      }
-      // stage kt + 1 landed (this wave's copies), then everyone's; nobody
-      // reads stage kt any more
-      wait_vm<0>();
-      __syncthreads();
-      if constexpr (kInterleave) {
-        load_step<kAKMajor, kBKMajor>(la, lb, smem + ((kt + 1) & 1) * kStage, 0, wy, wx, lane, fa[0], fb[0]);
-        __builtin_amdgcn_sched_barrier(0);
-        // past the last stage the copies read nothing and fill the free buffer with zeros
-        const bool more = kt + 2 < nk;
-        const uint32_t dst = lds0 + (kt & 1) * kStage;
-        const int64_t kn = k0 + (int64_t)(kt + 2) * kBK;
-        const auto sa = la.stage(kn, more);
-        const auto sb = lb.stage(kn, more);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            acc[i][j] = mma_chunk<__bf16>(fa[1][i], fb[1][j], acc[i][j]);
-            const int u = 4 * i + j;
-            if (u < kLoads)
-              la.issue_one(sa, dst, u, wave);
-            else
-              lb.issue_one(sb, dst + kOp, u - kLoads, wave);
-          }
-#pragma unroll
-        for (int u = 0; u < 2 * kLoads; ++u) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // then one copy
-        }
-      } else {
-        if (kt + 2 < nk) {
-          const uint32_t dst = lds0 + (kt & 1) * kStage;
-          la.issue(dst, k0 + (int64_t)(kt + 2) * kBK, wave);
-          lb.issue(dst + kOp, k0 + (int64_t)(kt + 2) * kBK, wave);
-        }
-        load_step<kAKMajor, kBKMajor>(la, lb, smem + ((kt + 1) & 1) * kStage, 0, wy, wx, lane, fa[0], fb[0]);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_step(fa[1], fb[1], acc);
-      }
-    }
-    {
-      const char* cur = smem + ((nk - 1) & 1) * kStage;
-#pragma unroll
-      for (int s = 0; s < 3; ++s) {
-        load_step<kAKMajor, kBKMajor>(la, lb, cur, s + 1, wy, wx, lane, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        mma_step(fa[s & 1], fb[s & 1], acc);
-      }
-      mma_step(fa[1], fb[1], acc);
-    }
-    wait_vm<0>();
-    __syncthreads();  // stage buffers free
-  }
-};
-
+// One tile's pass over K.  LDS holds five 32 KiB operand slabs in a ring:
+// stage k's A tile sits in slab 2k mod 5, its B tile in slab 2k + 1 mod 5.
+// While stage k is multiplied, stage k + 1 is in flight or landed, and
+//   * A of stage k + 2 goes to the slab B of stage k - 1 left, its eight
+//     copies per wave spread over steps 0..2 of stage k (3, 3, 2);
+//   * B of stage k + 2 goes to the slab A of stage k leaves, one copy per
+//     two MFMAs of step 3, after the stage's only barrier.
+// So one stage's copies are spread over the whole stage instead of bunched
+// into its last step, and the in-order copy counter lets each wave wait for
+// exactly the stage it needs (the newest eight copies stay in flight).  The
+// copies are inline asm, placed by scheduling barriers: with the compiler's
+// own LDS-copy builtin it would wait for every copy before each transposing
+// LDS read.  Each step's fragment reads are split, the A half before the
+// step's MFMAs and the B half after eight of them, so no more than 8 (K-
+// contiguous) or 16 (K-major) LDS reads are outstanding at a time.
+// Copies past the last stage read nothing and write zeros into free slabs.
 template <bool kAKMajor, bool kBKMajor>
 __device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, int64_t m0, const Operand<__bf16>& B,
                                          int64_t n0, int64_t k0, int64_t k1, f32x16 (&acc)[4][4]) {
-  Pipe<kAKMajor, kBKMajor> p;
-  p.init(A, m0, B, n0, k0, k1);
-  p.prologue(lds_addr(smem));
-  p.run(smem, acc);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wy = wave >> 1, wx = wave & 1;
+  LoaderT<kAKMajor> la;
+  LoaderT<kBKMajor> lb;
+  la.init(A, m0, wave, lane);
+  lb.init(B, n0, wave, lane);
+  int nk = (int)((k1 - k0 + kBK - 1) / kBK);
+  if (nk < 0) nk = 0;
+  const uint32_t lds0 = lds_addr(smem);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  if (nk <= 0) return;
+  {
+    const auto a0 = la.stage(k0, true);
+    const auto b0 = lb.stage(k0, true);
+    const auto a1 = la.stage(k0 + kBK, nk > 1);
+    const auto b1 = lb.stage(k0 + kBK, nk > 1);
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) la.issue(a0, lds0, q, wave);
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) lb.issue(b0, lds0 + kSlab, q, wave);
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) la.issue(a1, lds0 + 2 * kSlab, q, wave);
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) lb.issue(b1, lds0 + 3 * kSlab, q, wave);
+  }
+  wait_barrier<2 * kLoads>();  // stage 0 is in
+
+  u32x4 fa[2][4], fb[2][4];
+  uint32_t sa = 0;  // slab of A for the current stage
+  load_frags<kAKMajor>(la, smem, 0, wy, lane, fa[0]);
+  load_frags<kBKMajor>(lb, smem + kSlab, 0, wx, lane, fb[0]);
+  // every iteration of this loop has a next stage; the last stage follows
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    const char* ta = smem + sa * kSlab;
+    const char* tb = smem + mod5(sa + 1) * kSlab;
+    const bool more = kt + 2 < nk;
+    const int64_t kn = k0 + (int64_t)(kt + 2) * kBK;
+    const auto sta = la.stage(kn, more);
+    const uint32_t dsta = lds0 + mod5(sa + 4) * kSlab;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      load_frags<kAKMajor>(la, ta, s + 1, wy, lane, fa[(s + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      const int nq = s < 2 ? 3 : 2;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (u == 8) {
+          __builtin_amdgcn_sched_barrier(0);
+          load_frags<kBKMajor>(lb, tb, s + 1, wx, lane, fb[(s + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        acc[u >> 2][u & 3] = mma_chunk<__bf16>(fa[s & 1][u >> 2], fb[s & 1][u & 3], acc[u >> 2][u & 3]);
+        if ((u == 3 || u == 8 || u == 13) && (u - 3) / 5 < nq) {
+          __builtin_amdgcn_sched_barrier(0);
+          la.issue(sta, dsta, 3 * s + (u - 3) / 5, wave);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // all but this stage's eight A copies landed, so stage kt + 1 is in;
+    // after the barrier nobody reads stage kt any more
+    wait_barrier<kLoads>();
+    const uint32_t sn = mod5(sa + 2);
+    load_frags<kAKMajor>(la, smem + sn * kSlab, 0, wy, lane, fa[0]);
+    load_frags<kBKMajor>(lb, smem + mod5(sn + 1) * kSlab, 0, wx, lane, fb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    const auto stb = lb.stage(kn, more);
+    const uint32_t dstb = lds0 + sa * kSlab;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      acc[u >> 2][u & 3] = mma_chunk<__bf16>(fa[1][u >> 2], fb[1][u & 3], acc[u >> 2][u & 3]);
+      if (u & 1) {
+        __builtin_amdgcn_sched_barrier(0);
+        lb.issue(stb, dstb, u >> 1, wave);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    sa = sn;
+  }
+  {
+    const char* ta = smem + sa * kSlab;
+    const char* tb = smem + mod5(sa + 1) * kSlab;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      load_frags<kAKMajor>(la, ta, s + 1, wy, lane, fa[(s + 1) & 1]);
+      load_frags<kBKMajor>(lb, tb, s + 1, wx, lane, fb[(s + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        acc[u >> 2][u & 3] = mma_chunk<__bf16>(fa[s & 1][u >> 2], fb[s & 1][u & 3], acc[u >> 2][u & 3]);
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      acc[u >> 2][u & 3] = mma_chunk<__bf16>(fa[1][u >> 2], fb[1][u & 3], acc[u >> 2][u & 3]);
+  }
+  wait_vm<0>();
+  __syncthreads();  // the slabs are free for the caller
 }
 
 }  // namespace pipe
 
 // acc = A[m0:m0+256, k0:k1) * B[n0:n0+256, k0:k1)^T: the direct-to-LDS
 // pipeline for bf16, the register-staged loop for fp32.
-static_assert(2 * pipe::kStage <= kLdsBytes, "LDS");
-constexpr int kGemmLdsBytes = kLdsBytes;
+static_assert(kLdsBytes <= pipe::kRingBytes, "LDS");
+constexpr int kGemmLdsBytes = pipe::kRingBytes;
 
 // Tile-order group size (consecutive tile rows walked column by column).
 #ifndef FLCE_TILE_GROUP
