@@ -92,10 +92,11 @@ def gpu_bench(w, steps, warmup, forward=True):
     wall_ms = (wall1 - wall0) * 1e3 / steps
 
     # forward only (evaluation path), timed separately and reported as context
-    fwd_ms = orpo = None
+    fwd_ms = orpo = eager = None
     if forward:
         fwd_ms = time_forward(flce, w, Xd, Wd, yd, steps, stream, float(out[0].item()))
         orpo = time_orpo(flce, w, Xd, Wd, yd, stream)
+        eager = time_torch_eager(w, Xd, Wd, yd, stream, float(out[0].item()))
     err = int(out[3].item())
     if err != 0:
         raise RuntimeError(f"device reported error flag {err}")
@@ -106,7 +107,7 @@ def gpu_bench(w, steps, warmup, forward=True):
     log(f"[bench] {ms:.3f} ms/step (wall {wall_ms:.3f}); kernels: "
         + ", ".join(f"{k} {v['ms_per_step']:.3f}" for k, v in kernels.items()))
     return {"ms": ms, "ms_min": per_step[0], "ms_median": per_step[len(per_step) // 2], "fwd_ms": fwd_ms,
-            "orpo": orpo, "C": C, "ws_bytes": ws_bytes, "peak_extra": peak_extra,
+            "orpo": orpo, "eager": eager, "C": C, "ws_bytes": ws_bytes, "peak_extra": peak_extra,
             "loss": loss,
             "kernels": kernels,
             "cus": props.multi_processor_count, "arch": getattr(props, "gcnArchName", "?")}
@@ -136,6 +137,52 @@ def time_forward(flce, w, Xd, Wd, yd, steps, stream, loss_fwd_bwd):
         raise RuntimeError("forward-only loss differs from the fwd+bwd loss")
     log(f"[bench] forward only: {fwd_ms:.3f} ms/step")
     return fwd_ms
+
+
+def time_torch_eager(w, Xd, Wd, yd, stream, loss_flce, reps=3):
+    """The unfused composition in plain PyTorch on the GPU (context only, the
+    analogue of the unfused baseline the pages compare against): full logits
+    X W^T in the input dtype, cross-entropy in fp32, autograd backward.
+    ms per fwd+bwd, peak extra bytes over the inputs, and its loss."""
+    import torch
+    import torch.nn.functional as F
+
+    Xr = Xd.detach().clone().requires_grad_(True)
+    Wr = Wd.detach().clone().requires_grad_(True)
+
+    def step():
+        Xr.grad = None
+        Wr.grad = None
+        logits = torch.mm(Xr, Wr.t())  # one 2-D product, no batched path
+        loss = F.cross_entropy(logits.float(), yd, ignore_index=w.ignore_index)
+        loss.backward()
+        return loss
+
+    step()
+    torch.cuda.synchronize()
+    Xr.grad = None
+    Wr.grad = None
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    loss = step()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        loss = step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    le = float(loss.item())
+    del Xr, Wr, loss
+    torch.cuda.empty_cache()
+    log(f"[bench] torch eager (unfused) fwd+bwd: {ms:.3f} ms/step, peak extra {peak / 2**30:.2f} GiB, "
+        f"loss {le:.6f} (fused {loss_flce:.6f})")
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.BT / (ms * 1e-3), 1),
+            "peak_extra_bytes": int(peak), "loss": le,
+            "what": "torch.mm(X, W.t()) in the input dtype + F.cross_entropy(fp32 logits) + autograd backward"}
 
 
 def time_orpo(flce, w, Xd, Wd, yd, stream, seq_len=1024, reps=3):
@@ -215,10 +262,10 @@ def copy_calibration(nbytes=256 << 20, reps=3):
     log(f"[bench] copy calibration: {reps} x {nbytes} bytes read + written")
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary (profiles/hbm_traffic.json), or None if the kernel sources changed
-    since the counters were taken (hash of linear_cross_entropy_05_amd/csrc)."""
+def profiled(kernel: str):
+    """The committed rocprofv3 counter record of `kernel`
+    (profiles/hbm_traffic.json), or None if the kernel sources changed since
+    the counters were taken (hash of linear_cross_entropy_05_amd/csrc)."""
     import glob
     import hashlib
 
@@ -233,8 +280,23 @@ def measured_traffic(kernel: str):
             h.update(f.read())
     if h.hexdigest()[:16] != t.get("source_sha256"):
         return None
-    k = t.get("kernels", {}).get(kernel)
+    return t.get("kernels", {}).get(kernel)
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy)."""
+    k = profiled(kernel)
     return int(k["bytes_per_launch"]) if k else None
+
+
+def measured_mfma(kernel: str):
+    """MFMA busy fraction and the clock the kernel ran at, from the
+    SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE counter pass."""
+    k = profiled(kernel)
+    if not k or "mfma_busy_pct" not in k:
+        return None
+    return {"kernel": kernel, "mfma_busy_pct": k["mfma_busy_pct"], "clock_ghz": k["clock_ghz"],
+            "source": "profiles/hbm_traffic.json (rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE)"}
 
 
 def roofline(w, r):
@@ -295,7 +357,7 @@ def main(argv=None):
     ap.add_argument("--config", default="llama3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-forward", action="store_true",
-                    help="skip the context timings (forward only, ORPO, logits-only CE)")
+                    help="skip the context timings (forward only, ORPO, unfused torch, logits-only CE)")
     ap.add_argument("--ce-only", action="store_true",
                     help="time only the logits-only CE on the Gemma shape (for its profile)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
@@ -344,8 +406,10 @@ def main(argv=None):
         "workspace_bytes": int(r["ws_bytes"]),
         "dominant_kernel": dom,
         "roofline": roof,
+        "mfma_counters": measured_mfma(dom),
         "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in r["kernels"].items()},
         "orpo": r["orpo"],
+        "torch_eager": r["eager"],
         "ce_inplace": ce,
         "forward_only": None if r["fwd_ms"] is None else {
             "ms_per_step": round(r["fwd_ms"], 4), "tokens_per_s": round(w.BT / (r["fwd_ms"] * 1e-3), 1),
