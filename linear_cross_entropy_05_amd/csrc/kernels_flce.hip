@@ -455,18 +455,21 @@ __global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
   char* st = smem + wave * (32 * 512);
   const int t = lane & 31, hh = lane >> 5;
   const int hcol = (wave >> 1) * 128 + 4 * t;  // this lane's 4 columns in the staged pass
+  // whole tile inside dW: no per-lane guards, so the compiler can batch the
+  // LDS reads and global accesses instead of branching around each one
+  const bool full = vlim == kTile && hlim == kTile;
+  // half-block hb = rows 16 (hb % 2) .. + 15 of block hb / 2; lane row k of
+  // it is dW row vrow + 2 k + hh
+  auto row_of = [&](int hb, int k) { return (wave & 1) * 128 + 32 * (hb >> 1) + 16 * (hb & 1) + 2 * k + hh; };
+  auto load_old = [&](int hb, f32x4 (&o)[8]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int vrow = (wave & 1) * 128 + 32 * j;  // first row of this block
-    f32x4 old[16];
-    if (!a.first) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int v = vrow + 2 * k + hh;
-        old[k] = (v < vlim && hcol < hlim) ? *reinterpret_cast<const f32x4*>(base + ((uint32_t)v * H + (uint32_t)hcol))
-                                           : f32x4{};
-      }
+    for (int k = 0; k < 8; ++k) {
+      const int v = row_of(hb, k);
+      const f32x4* p = reinterpret_cast<const f32x4*>(base + ((uint32_t)v * H + (uint32_t)hcol));
+      o[k] = full ? *p : (v < vlim && hcol < hlim) ? *p : f32x4{};
     }
+  };
+  auto stage = [&](int j) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -475,13 +478,43 @@ __global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
         *reinterpret_cast<f32x4*>(st + t * 512 + ((c ^ t) << 4)) =
             f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
       }
+  };
+  // stores half-block hb; `d` holds its old rows (added to) or is scratch
+  auto store_half = [&](int hb, f32x4 (&d)[8], bool add) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int r = 2 * k + hh, v = vrow + r;
-      f32x4 d = *reinterpret_cast<const f32x4*>(st + r * 512 + ((t ^ r) << 4));
-      if (!a.first) d += old[k];
-      if (v < vlim && hcol < hlim)
-        __builtin_nontemporal_store(d, reinterpret_cast<f32x4*>(base + ((uint32_t)v * H + (uint32_t)hcol)));
+    for (int k = 0; k < 8; ++k) {
+      const int r = 16 * (hb & 1) + 2 * k + hh;
+      const f32x4 z = *reinterpret_cast<const f32x4*>(st + r * 512 + ((t ^ r) << 4));
+      d[k] = add ? d[k] + z : z;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int v = row_of(hb, k);
+      if (full || (v < vlim && hcol < hlim))
+        __builtin_nontemporal_store(d[k], reinterpret_cast<f32x4*>(base + ((uint32_t)v * H + (uint32_t)hcol)));
+    }
+  };
+  f32x4 x[8], y[8];
+  if (a.first) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      stage(j);
+      store_half(2 * j, x, false);
+      store_half(2 * j + 1, y, false);
+    }
+  } else {
+    // two half-blocks of old rows in flight: the rows of half-block h + 1 are
+    // requested before the stores of half-block h, so waiting for them never
+    // waits for those stores (loads and stores complete in issue order)
+    load_old(0, x);
+    load_old(1, y);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      stage(j);
+      store_half(2 * j, x, true);
+      if (j < 3) load_old(2 * j + 2, x);
+      store_half(2 * j + 1, y, true);
+      if (j < 3) load_old(2 * j + 3, y);
     }
   }
 }
