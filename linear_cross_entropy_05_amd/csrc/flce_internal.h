@@ -19,6 +19,9 @@ struct Layout {
   int64_t nvt;      // vocabulary tiles of the logits GEMM (ceil(V / 256)); statistics per half tile
   int64_t splits;   // K splits of the dX GEMM
   int64_t esize;    // bytes per element of X, W and the chunk
+  int64_t ldxt;     // bf16: elements between rows of the transposed token chunk X_c^T [H, ldxt]
+  // X_c^T shares the statistics region (off_part): the statistics are dead
+  // once the gradient pass has run, and X_c^T is only read by the dW product
   size_t off_nvalid, off_lse, off_rowloss, off_part, off_chunk, off_dxpart, total;
 };
 

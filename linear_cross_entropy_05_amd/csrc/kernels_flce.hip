@@ -421,12 +421,34 @@ __global__ __launch_bounds__(256) void k_dx_reduce(const float* __restrict__ par
 
 template <typename T>
 struct DwArgs {
-  Operand<T> G;  // chunk buffer read K-major ([rows = K][ldz]): the GEMM's B (columns v)
-  Operand<T> X;  // chunk tokens [rows = K][H], read K-major: the GEMM's A (rows h)
+  Operand<T> G;   // chunk buffer read K-major ([rows = K][ldz]): the GEMM's B (columns v)
+  Operand<T> X;   // fp32: chunk tokens [rows = K][H], read K-major: the GEMM's A (rows h)
+  Operand<T> XT;  // bf16: the chunk transposed, [H][ldxt], K-contiguous: the GEMM's A
   int64_t V, H, rows, nvt, nht;
-  float* dw;     // [V, H]
+  float* dw;      // [V, H]
   int first;
 };
+
+// X_c^T[h][c] = X_c[c][h] for c < rows, 0 for rows <= c < ldxt (the K tail
+// of the dW product reads whole 16-byte chunks, so the padding must be
+// finite).  64 x 64 tiles through LDS; both global passes are coalesced.
+__global__ __launch_bounds__(256) void k_transpose_chunk(const uint16_t* __restrict__ X, int64_t rows, int64_t H,
+                                                         uint16_t* __restrict__ XT, int64_t ldxt) {
+  __shared__ uint16_t tile[64][66];
+  const int64_t c0 = (int64_t)blockIdx.x * 64, h0 = (int64_t)blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int r = ty; r < 64; r += 4) {
+    const int64_t c = c0 + r, h = h0 + tx;
+    tile[r][tx] = (c < rows && h < H) ? X[c * H + h] : (uint16_t)0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = ty; r < 64; r += 4) {
+    const int64_t h = h0 + r, c = c0 + tx;
+    if (h < H && c < ldxt) XT[h * ldxt + c] = tile[tx][r];
+  }
+}
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
@@ -438,7 +460,10 @@ __global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
   // X_chunk^T as the A operand (rows h) and G^T as B (columns v): each lane
   // then holds four consecutive h of one dW row
   f32x16 acc[4][4];
-  gemm_mainloop<T, true, true>(smem, a.X, h0, a.G, v0, 0, a.rows, acc);
+  if constexpr (sizeof(T) == 2)
+    gemm_mainloop<T, false, true>(smem, a.XT, h0, a.G, v0, 0, a.rows, acc);
+  else
+    gemm_mainloop<T, true, true>(smem, a.X, h0, a.G, v0, 0, a.rows, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // accumulator (i, j, e): h = h0 + (wave / 2) 128 + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4,
@@ -599,7 +624,12 @@ Layout make_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int d
   L.off_rowloss = o;
   o = align256(o + (size_t)(BT > 0 ? BT : 1) * 4);
   L.off_part = o;
-  o = align256(o + (size_t)C * 2 * L.nvt * 8);
+  L.ldxt = (C + 63) / 64 * 64;
+  {
+    const size_t stats = (size_t)C * 2 * L.nvt * 8;
+    const size_t xt = dtype == 1 ? (size_t)H * L.ldxt * 2 : 0;
+    o = align256(o + (stats > xt ? stats : xt));
+  }
   L.off_chunk = o;
   o = align256(o + chunk_bytes);
   L.off_dxpart = o;
@@ -748,6 +778,8 @@ static hipError_t chunk_impl(const Layout& L, const T* X, const T* W, const int6
   DwArgs<T> wa;
   wa.G = Operand<T>{z, L.ldz, rows, L.ldz};
   wa.X = Operand<T>{Xc, H, rows, H};
+  T* xt = reinterpret_cast<T*>(ws + L.off_part);  // the statistics are dead after the gradient pass
+  wa.XT = Operand<T>{xt, L.ldxt, H, rows};
   wa.V = V;
   wa.H = H;
   wa.rows = rows;
@@ -756,7 +788,10 @@ static hipError_t chunk_impl(const Layout& L, const T* X, const T* W, const int6
   wa.dw = dW;
   wa.first = first ? 1 : 0;
   {
-    ProfScope ps(kPhaseDw, s);
+    ProfScope ps(kPhaseDw, s);  // bf16: the chunk transpose is counted with the dW product
+    if constexpr (sizeof(T) == 2)
+      hipLaunchKernelGGL(k_transpose_chunk, dim3((unsigned)(L.ldxt / 64), (unsigned)((H + 63) / 64)), dim3(256), 0, s,
+                         reinterpret_cast<const uint16_t*>(Xc), rows, H, reinterpret_cast<uint16_t*>(xt), L.ldxt);
     hipLaunchKernelGGL(k_dw<T>, dim3((unsigned)(wa.nvt * wa.nht)), dim3(kThreads), 0, s, wa);
   }
   return hipGetLastError();
