@@ -154,7 +154,7 @@ size_t ce_workspace_bytes(int64_t BT, int64_t V);
  * kernel of the same review page (主な発見): online softmax per row, then the
  * fp32 logits [BT, V] are overwritten by d loss / d logits
  * = (softmax - onehot) / N (rows with ignored targets become 0).
- *   logits   [BT, V] float, 4-byte aligned (any V)
+ *   logits   [BT, V] float, 4-byte aligned; 1 <= V < 2^31 (status 1 otherwise)
  *   targets, ignore_index, loss, row_loss, err_flag, stream: as above. */
 int ce_fwd_bwd_inplace(float* logits, const int64_t* targets, int64_t BT, int64_t V, int64_t ignore_index,
                        float* loss, float* row_loss, void* workspace, size_t workspace_bytes, int32_t* err_flag,

@@ -231,7 +231,7 @@ size_t ce_workspace_bytes(int64_t BT, int64_t V) {
 int ce_fwd_bwd_inplace(float* logits, const int64_t* targets, int64_t BT, int64_t V, int64_t ignore_index,
                        float* loss, float* row_loss, void* workspace, size_t workspace_bytes, int32_t* err_flag,
                        void* stream) {
-  if (BT < 0 || V <= 0 || BT > INT32_MAX) return FLCE_ERR_ARG;
+  if (BT < 0 || V <= 0 || BT > INT32_MAX || V > INT32_MAX) return FLCE_ERR_ARG;
   if (!loss || !workspace || !err_flag) return FLCE_ERR_ARG;
   if (BT > 0 && (!logits || !targets)) return FLCE_ERR_ARG;
   if ((logits && !aligned(logits, 4)) || (targets && !aligned(targets, 8)) || !aligned(workspace, 256) ||

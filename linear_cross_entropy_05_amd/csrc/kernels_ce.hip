@@ -12,22 +12,23 @@
 #include <float.h>
 
 #include "flce_internal.h"
+#include "gemm_core.h"
 
 namespace flce {
 
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-// 1024 threads per row and 16 vector loads in flight per thread: a row's two
-// sweeps then follow each other closely enough that the second mostly hits
-// the MALL (measured on the 8192 x 256000 fp32 logits: 4.9 -> 4.3 ms)
+// One 1024-thread workgroup per row, one row per CU at a time.  Sweep 2 needs
+// the whole row again, so as much of it as fits stays on chip between the
+// sweeps: per thread kRegVec 16-byte vectors in registers and kLdsVec in LDS
+// (copied there straight from memory, no registers), 25 x 16 KiB = 400 KiB
+// of a row; only the rest is read a second time.
 constexpr int kCeThreads = 1024;
-constexpr int kUnroll = 16;
-// The first unrolled iteration of a row (16 x 1024 vectors, 256 KiB) stays on
-// chip between the sweeps: 9 x 1024 vectors (144 KiB) in LDS, the other 7 in
-// registers.
-constexpr int kCacheBlocks = 9;
-constexpr int kCacheVec = kCacheBlocks * kCeThreads;
+constexpr int kRegVec = 16;
+constexpr int kLdsVec = 9;  // 144 KiB of LDS
+constexpr int kKeepVec = kRegVec + kLdsVec;
+constexpr int kStream = 4;  // loads in flight per thread over the rest of the row
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -61,53 +62,74 @@ struct Online {
 
 }  // namespace
 
+// Element indices within a row are 32-bit: the launcher rejects V >= 2^31.
 __global__ __launch_bounds__(kCeThreads) void k_ce_rows(float* __restrict__ logits, const int64_t* __restrict__ y,
-                                                        int64_t V, int64_t ign, const int32_t* __restrict__ nvalid,
+                                                        int64_t V64, int64_t ign, const int32_t* __restrict__ nvalid,
                                                         float* __restrict__ rowloss) {
   __shared__ float red_m[kCeThreads / 64], red_s[kCeThreads / 64];
-  __shared__ f32x4 cache[kCacheVec];  // first vectors of the row, kept for sweep 2
+  __shared__ f32x4 cache[kLdsVec * kCeThreads];  // slot u of thread i: vector i + (kRegVec + u) T of the body
   __shared__ float lse_sh;
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x;
-  float* row = logits + r * V;
-  const int64_t t = y[r];
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int V = (int)V64;
+  float* row = logits + r * V64;
+  const int64_t t64 = y[r];
 
   // split the row into a scalar head (up to 16-byte alignment), a vector body and a scalar tail
-  const int64_t mis = (int64_t)(((uintptr_t)row >> 2) & 3);
-  int64_t head = mis ? 4 - mis : 0;
+  const int mis = (int)(((uintptr_t)row >> 2) & 3);
+  int head = mis ? 4 - mis : 0;
   if (head > V) head = V;
-  const int64_t nvec = (V - head) / 4;
-  const int64_t tail0 = head + 4 * nvec;
+  const int nvec = (V - head) / 4;
+  const int tail0 = head + 4 * nvec;
   f32x4* body = reinterpret_cast<f32x4*>(row + head);
 
-  if (t == ign) {
-    for (int64_t i = tid; i < head; i += kCeThreads) row[i] = 0.f;
-    for (int64_t i = tid; i < nvec; i += kCeThreads) body[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int64_t i = tail0 + tid; i < V; i += kCeThreads) row[i] = 0.f;
+  if (t64 == ign) {
+    for (int i = tid; i < head; i += kCeThreads) row[i] = 0.f;
+    for (int i = tid; i < nvec; i += kCeThreads) body[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = tail0 + tid; i < V; i += kCeThreads) row[i] = 0.f;
     if (tid == 0) rowloss[r] = 0.f;
     return;
   }
+  // the target as a body-relative element index (out-of-range targets were
+  // flagged by the count pass and match no element)
+  const int t = (t64 >= 0 && t64 < V64) ? (int)t64 : -1;
 
-  // sweep 1 (the first kCacheVec vectors of the body also go to LDS for sweep 2)
+  // sweep 1.  The LDS part is copied first (vectors past the body read as
+  // zero and are never used), then the register part is loaded, then the
+  // rest of the row streams through.
+  {
+    const u32x4 rs = pipe::rsrc_words(body, (int64_t)nvec * 16);
+    const uint32_t base = pipe::lds_addr(reinterpret_cast<const char*>(cache)) + 1024u * (uint32_t)wave;
+#pragma unroll
+    for (int u = 0; u < kLdsVec; ++u)
+      pipe::dma16(rs, base + (uint32_t)(u * kCeThreads * 16), (uint32_t)((tid + (kRegVec + u) * kCeThreads) * 16), 0);
+  }
   Online o{-FLT_MAX, 0.f};
-  f32x4 kept[kUnroll - kCacheBlocks];  // the rest of the first iteration, in registers
-  for (int64_t i = tid; i < head; i += kCeThreads) o.add1(row[i]);
-  int64_t i = tid;
-  for (; i + (kUnroll - 1) * kCeThreads < nvec; i += kUnroll * kCeThreads) {
-    f32x4 x[kUnroll];
+  f32x4 kept[kRegVec];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) x[u] = body[i + u * kCeThreads];
-    if (i < kCacheVec) {
+  for (int u = 0; u < kRegVec; ++u) {
+    const int v = tid + u * kCeThreads;
+    kept[u] = v < nvec ? body[v] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int i = tid; i < head; i += kCeThreads) o.add1(row[i]);
 #pragma unroll
-      for (int u = 0; u < kCacheBlocks; ++u) cache[i + u * kCeThreads] = x[u];
+  for (int u = 0; u < kRegVec; ++u)
+    if (tid + u * kCeThreads < nvec) o.add4(kept[u]);
+  int i = tid + kKeepVec * kCeThreads;
+  for (; i + (kStream - 1) * kCeThreads < nvec; i += kStream * kCeThreads) {
+    f32x4 x[kStream];
 #pragma unroll
-      for (int u = kCacheBlocks; u < kUnroll; ++u) kept[u - kCacheBlocks] = x[u];
-    }
+    for (int u = 0; u < kStream; ++u) x[u] = body[i + u * kCeThreads];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) o.add4(x[u]);
+    for (int u = 0; u < kStream; ++u) o.add4(x[u]);
   }
   for (; i < nvec; i += kCeThreads) o.add4(body[i]);
-  for (int64_t k = tail0 + tid; k < V; k += kCeThreads) o.add1(row[k]);
+  for (int k = tail0 + tid; k < V; k += kCeThreads) o.add1(row[k]);
+  pipe::wait_vm<0>();  // this thread's LDS slots have landed
+#pragma unroll
+  for (int u = 0; u < kLdsVec; ++u)
+    if (tid + (kRegVec + u) * kCeThreads < nvec) o.add4(cache[u * kCeThreads + tid]);
 
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -123,42 +145,44 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_rows(float* __restrict__ logi
     Online a{red_m[0], red_s[0]};
     for (int w = 1; w < kCeThreads / 64; ++w) a.merge(red_m[w], red_s[w]);
     const float lse = a.m + logf(a.s);
-    const float zt = (t >= 0 && t < V) ? row[t] : 0.f;
+    const float zt = t >= 0 ? row[t] : 0.f;
     rowloss[r] = lse - zt;
     lse_sh = lse;
   }
   __syncthreads();
 
-  // sweep 2
+  // sweep 2: gradients over the logits; they are not read again here, so
+  // they stream past the caches
   const int n = *nvalid;
   const float inv = 1.f / (float)(n > 0 ? n : 1);
   const float lb = lse_sh * kLog2e;
-  auto g1 = [&](float z, int64_t v) { return (ex2(fmaf(z, kLog2e, -lb)) - (v == t ? 1.f : 0.f)) * inv; };
-  for (int64_t k = tid; k < head; k += kCeThreads) row[k] = g1(row[k], k);
-  i = tid;
-  for (; i + (kUnroll - 1) * kCeThreads < nvec; i += kUnroll * kCeThreads) {
-    f32x4 x[kUnroll];
-    if (i < kCacheVec) {
+  auto g1 = [&](float z, int v) { return (ex2(fmaf(z, kLog2e, -lb)) - (v == t ? 1.f : 0.f)) * inv; };
+  auto g4 = [&](f32x4 x, int vi) {
+    const int v = head + 4 * vi;
+    return f32x4{g1(x[0], v), g1(x[1], v + 1), g1(x[2], v + 2), g1(x[3], v + 3)};
+  };
+  for (int k = tid; k < head; k += kCeThreads) row[k] = g1(row[k], k);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) x[u] = u < kCacheBlocks ? cache[i + u * kCeThreads] : kept[u - kCacheBlocks];
-    } else {
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) x[u] = body[i + u * kCeThreads];
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t v = head + 4 * (i + u * kCeThreads);
-      // gradients are not read again here: stream them past the caches
-      __builtin_nontemporal_store(f32x4{g1(x[u][0], v), g1(x[u][1], v + 1), g1(x[u][2], v + 2), g1(x[u][3], v + 3)},
-                                  &body[i + u * kCeThreads]);
-    }
+  for (int u = 0; u < kRegVec; ++u) {
+    const int v = tid + u * kCeThreads;
+    if (v < nvec) __builtin_nontemporal_store(g4(kept[u], v), &body[v]);
   }
-  for (; i < nvec; i += kCeThreads) {
-    const f32x4 x = body[i];
-    const int64_t v = head + 4 * i;
-    body[i] = f32x4{g1(x[0], v), g1(x[1], v + 1), g1(x[2], v + 2), g1(x[3], v + 3)};
+#pragma unroll
+  for (int u = 0; u < kLdsVec; ++u) {
+    const int v = tid + (kRegVec + u) * kCeThreads;
+    if (v < nvec) __builtin_nontemporal_store(g4(cache[u * kCeThreads + tid], v), &body[v]);
   }
-  for (int64_t k = tail0 + tid; k < V; k += kCeThreads) row[k] = g1(row[k], k);
+  i = tid + kKeepVec * kCeThreads;
+  for (; i + (kStream - 1) * kCeThreads < nvec; i += kStream * kCeThreads) {
+    f32x4 x[kStream];
+#pragma unroll
+    for (int u = 0; u < kStream; ++u) x[u] = body[i + u * kCeThreads];
+#pragma unroll
+    for (int u = 0; u < kStream; ++u)
+      __builtin_nontemporal_store(g4(x[u], i + u * kCeThreads), &body[i + u * kCeThreads]);
+  }
+  for (; i < nvec; i += kCeThreads) body[i] = g4(body[i], i);
+  for (int k = tail0 + tid; k < V; k += kCeThreads) row[k] = g1(row[k], k);
 }
 
 hipError_t launch_ce_rows(float* logits, const int64_t* y, int64_t BT, int64_t V, int64_t ign, const int32_t* nvalid,

@@ -160,6 +160,7 @@ def test_ce_host_argument_checks(lib):
     f = lib.ce_fwd_bwd_inplace
     assert f(vp(16), vp(16), -1, 10, -100, vp(16), vp(0), vp(256), 4096, vp(16), vp(0)) == 1
     assert f(vp(16), vp(16), 4, 0, -100, vp(16), vp(0), vp(256), 4096, vp(16), vp(0)) == 1
+    assert f(vp(16), vp(16), 4, 1 << 31, -100, vp(16), vp(0), vp(256), 4096, vp(16), vp(0)) == 1  # V >= 2^31
     assert f(vp(0), vp(16), 4, 10, -100, vp(16), vp(0), vp(256), 4096, vp(16), vp(0)) == 1
     assert f(vp(16), vp(16), 4, 10, -100, vp(0), vp(0), vp(256), 4096, vp(16), vp(0)) == 1
     assert f(vp(18), vp(16), 4, 10, -100, vp(16), vp(0), vp(256), 4096, vp(16), vp(0)) == 8

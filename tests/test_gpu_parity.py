@@ -158,7 +158,7 @@ def run_ce(logits_cpu, y, ignore_index=-100):
     return float(loss.item()), L.cpu(), rl.cpu()
 
 
-@pytest.mark.parametrize("V", [1, 7, 1001, 4096, 50257])
+@pytest.mark.parametrize("V", [1, 7, 1001, 4096, 50257, 65539, 102401, 150001])
 def test_ce_inplace_matches_oracle(V):
     g = torch.Generator().manual_seed(V)
     BT = 37
