@@ -318,8 +318,7 @@ __global__ __launch_bounds__(256) void k_grad(T* __restrict__ z, int64_t ldz, in
   }
   const float l = lse[c];
   const float2* pc = part + c * nvh;
-  for (int64_t v = (int64_t)threadIdx.x * E; v < ldz; v += 256 * E) {
-    u32x4 d = *reinterpret_cast<const u32x4*>(row + v);
+  auto grad16 = [&](u32x4 d, int64_t v) {
     const int64_t h = v / 128;
     const float lb = (l - (h < nvh ? pc[h].x : 0.f)) * kLog2e;
     if constexpr (sizeof(T) == 2) {
@@ -337,8 +336,23 @@ __global__ __launch_bounds__(256) void k_grad(T* __restrict__ z, int64_t ldz, in
                        grad1(zf.z, lb, v + 2, t, V, inv), grad1(zf.w, lb, v + 3, t, V, inv)};
       d = __builtin_bit_cast(u32x4, g);
     }
-    *reinterpret_cast<u32x4*>(row + v) = d;
+    return d;
+  };
+  // four 16-byte loads in flight per thread; the gradient is read next by
+  // the dX and dW products from memory (the chunk is far larger than the
+  // caches), so the stores stream past them
+  constexpr int kU = 4;
+  int64_t v = (int64_t)threadIdx.x * E;
+  for (; v + (kU - 1) * 256 * E < ldz; v += kU * 256 * E) {
+    u32x4 d[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) d[u] = *reinterpret_cast<const u32x4*>(row + v + u * 256 * E);
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      __builtin_nontemporal_store(grad16(d[u], v + u * 256 * E), reinterpret_cast<u32x4*>(row + v + u * 256 * E));
   }
+  for (; v < ldz; v += 256 * E)
+    __builtin_nontemporal_store(grad16(*reinterpret_cast<const u32x4*>(row + v), v), reinterpret_cast<u32x4*>(row + v));
 }
 
 // ---- dX = G W ---------------------------------------------------------------
