@@ -72,8 +72,11 @@ int64_t flce_chunk_tokens(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens
 
 /* Bytes of device workspace flce_fwd_bwd needs for these sizes: one logits
  * chunk (chunk x round_up(V, 256) elements of the dtype) plus per-token and
- * per-tile statistics (O(chunk x V / 256) floats) and, when the dX product
- * is split along the vocabulary, fp32 partials bounded by half the chunk.
+ * per-tile statistics (O(chunk x V / 256) floats; for bf16 the region is at
+ * least H x round_up(chunk, 64) x 2 bytes, as it also holds the transposed
+ * token chunk for the dW product once the statistics are consumed) and, when
+ * the dX product is split along the vocabulary, fp32 partials bounded by half
+ * the chunk.
  * This is the whole extra memory of the call.  Returns 0 for invalid args. */
 size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);
 
