@@ -34,8 +34,11 @@ Gradients are the chain rule through the token losses: the loss depends on Z
 only through l_i, so dL/dZ_i = (softmax_i - onehot_i) * w_i with
 w_i = dL/dl_i, and dX = G W, dW = G^T X (``flce_oracle.flce_ref`` with
 ``token_scale = w``).  Pinned in ``tests/test_oracle_orpo.py`` by a two-class
-closed form, beta = 0 (plain chosen-token cross-entropy), identical chosen and
-rejected sequences (r = 0), and central finite differences of the loss.
+closed form (also with every token repeated and an ignored token added, which
+leaves means over valid tokens unchanged), beta = 0 (plain chosen-token
+cross-entropy), identical chosen and rejected sequences (r = 0), and central
+finite differences of the loss; ``tests/test_oracle_orpo_mutants.py`` checks
+that these pins catch eight planted mistakes in a copy of the definition.
 """
 
 from __future__ import annotations

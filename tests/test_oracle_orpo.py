@@ -26,6 +26,23 @@ def test_two_class_closed_form():
     assert np.allclose(out["seq_logp"], [-sp(-v) for v in c], rtol=1e-14, atol=0)
 
 
+def test_two_class_repeated_tokens():
+    """The same closed form with every token repeated and an ignored token
+    added to each sequence: sequence scores are means over the valid tokens
+    and the NLL a mean over the chosen valid tokens, so nothing changes (a
+    sum in place of either mean would)."""
+    c = np.array([1.3, -0.4, 0.2, 2.0, 0.7, -1.1])
+    X = np.repeat(np.stack([c, np.zeros_like(c)], axis=1), 3, axis=0)
+    W = np.array([[0.0, 0.0], [1.0, 0.0]])
+    y = np.tile(np.array([1, 1, IGN]), 6)
+    beta = 0.25
+    out = orpo_ref(X, W, y, n_seq=6, beta=beta)
+    sp = lambda x: math.log1p(math.exp(-abs(x))) + max(x, 0.0)  # noqa: E731
+    expect = sum(sp(-c[p]) for p in range(3)) / 3 + beta * sum(sp(-(c[p] - c[3 + p])) for p in range(3)) / 3
+    assert abs(out["loss"] - expect) <= 1e-14 * expect, (out["loss"], expect)
+    assert np.allclose(out["seq_logp"], [-sp(-v) for v in c], rtol=1e-14, atol=0)
+
+
 def _case(seed, n_seq=4, T=3, H=4, V=6, n_ignore=2):
     r = np.random.default_rng(seed)
     X = r.standard_normal((n_seq * T, H))
