@@ -76,7 +76,7 @@ int64_t flce_chunk_tokens(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens
  * least H x round_up(chunk, 64) x 2 bytes, as it also holds the transposed
  * token chunk for the dW product once the statistics are consumed) and, when
  * the dX product is split along the vocabulary, fp32 partials bounded by half
- * the chunk.
+ * the chunk or 128 MiB, whichever is larger.
  * This is the whole extra memory of the call.  Returns 0 for invalid args. */
 size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);
 

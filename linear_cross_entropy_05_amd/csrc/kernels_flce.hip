@@ -583,13 +583,15 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static int64_t pick_splits(int64_t tiles, int64_t kstages, size_t part_bytes_per_split, size_t chunk_bytes) {
   // fewest K splits that fill the 256 CUs best, each split keeping >= 16
-  // stages of K, the fp32 partials within half the chunk buffer
+  // stages of K, the fp32 partials within half the chunk buffer or 128 MiB,
+  // whichever is larger (small chunks would otherwise leave most CUs idle)
   constexpr int64_t kCUs = 256;
+  const size_t cap = chunk_bytes / 2 > ((size_t)128 << 20) ? chunk_bytes / 2 : ((size_t)128 << 20);
   int64_t best = 1;
   double best_cost = (double)((tiles + kCUs - 1) / kCUs);
   for (int64_t s = 2; s <= 16; ++s) {
     if (kstages / s < 16) break;
-    if ((size_t)s * part_bytes_per_split > chunk_bytes / 2) break;
+    if ((size_t)s * part_bytes_per_split > cap) break;
     const double cost = (double)((tiles * s + kCUs - 1) / kCUs) / (double)s;
     if (cost < best_cost * 0.97) {
       best = s;
