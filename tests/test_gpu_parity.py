@@ -62,6 +62,15 @@ def test_bf16_wide_hidden_split_dx():
     check_against_oracle(si.small(300, 520, 5000, "bf16", seed=23), 300)
 
 
+@pytest.mark.parametrize("BT,H,V,chunk", [(130, 72, 300, 64), (257, 136, 777, 100), (65, 520, 1300, 0),
+                                           (513, 40, 5000, 200)])
+def test_bf16_shape_sweep(BT, H, V, chunk):
+    # hidden sizes and chunk lengths that are not multiples of 64 (the
+    # transposed token chunk of the dW product pads both), tiny and long
+    # vocabularies, several chunks with a ragged last one
+    check_against_oracle(si.small(BT, H, V, "bf16", seed=BT + H + V, w_std=0.05), chunk)
+
+
 def test_bf16_large_logits():
     # hidden states x3, as in the huge-vocabulary config: logits std ~3
     check_against_oracle(si.small(512, 768, 3000, "bf16", seed=24, x_scale=3.0, w_std=0.04), 0)
