@@ -289,14 +289,23 @@ def measured_traffic(kernel: str):
     return int(k["bytes_per_launch"]) if k else None
 
 
-def measured_mfma(kernel: str):
+PEAK_CLOCK_GHZ = 2.4  # the clock the published MFMA peak assumes
+
+
+def measured_mfma(kernel: str, achieved_tflops=None):
     """MFMA busy fraction and the clock the kernel ran at, from the
-    SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE counter pass."""
+    SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE counter pass, and the dense
+    bf16 peak scaled to that clock (the achieved rate against it when given)."""
     k = profiled(kernel)
     if not k or "mfma_busy_pct" not in k:
         return None
-    return {"kernel": kernel, "mfma_busy_pct": k["mfma_busy_pct"], "clock_ghz": k["clock_ghz"],
-            "source": "profiles/hbm_traffic.json (rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE)"}
+    peak_at_clock = PEAK_BF16_TFLOPS * k["clock_ghz"] / PEAK_CLOCK_GHZ
+    out = {"kernel": kernel, "mfma_busy_pct": k["mfma_busy_pct"], "clock_ghz": k["clock_ghz"],
+           "peak_at_clock_tflops": round(peak_at_clock, 1),
+           "source": "profiles/hbm_traffic.json (rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE)"}
+    if achieved_tflops is not None:
+        out["frac_at_clock"] = round(achieved_tflops / peak_at_clock, 4)
+    return out
 
 
 def roofline(w, r):
@@ -406,7 +415,7 @@ def main(argv=None):
         "workspace_bytes": int(r["ws_bytes"]),
         "dominant_kernel": dom,
         "roofline": roof,
-        "mfma_counters": measured_mfma(dom),
+        "mfma_counters": measured_mfma(dom, roof["achieved"] if roof["unit"] == "TFLOP/s" else None),
         "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in r["kernels"].items()},
         "orpo": r["orpo"],
         "torch_eager": r["eager"],
