@@ -468,7 +468,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char smem[kGemmLdsBytes];
   int64_t vt, ht;
-  grouped_tile(xcd_tile(blockIdx.x, a.nvt * a.nht), a.nvt, a.nht, kTileGroup, vt, ht);
+  // groups of 4 vocabulary tiles (measured ~1% faster than 8 for this product)
+  grouped_tile(xcd_tile(blockIdx.x, a.nvt * a.nht), a.nvt, a.nht, 4, vt, ht);
   const int64_t v0 = vt * kTile, h0 = ht * kTile;
 
   // X_chunk^T as the A operand (rows h) and G^T as B (columns v): each lane
