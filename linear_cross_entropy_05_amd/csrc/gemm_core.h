@@ -2,7 +2,8 @@
 // contractions of fused linear + cross-entropy:
 //   logits   Z^T[v,c] = sum_h W[v,h] X[c,h]     (both operands K-contiguous)
 //   dX       dX[c,h]  = sum_v G[c,v] W[v,h]     (W read K-major)
-//   dW       dW[v,h] += sum_c G[c,v] X[c,h]     (both read K-major)
+//   dW       dW[v,h] += sum_c G[c,v] X[c,h]     (G read K-major; bf16 X from a
+//                                                 transposed copy, K-contiguous)
 //
 // A workgroup of 256 threads (4 wave64s, 2 x 2) owns a 256 x 256 output tile;
 // each wave owns 128 x 128 = 4 x 4 MFMA 32x32 blocks (16 fp32 accumulators
