@@ -60,7 +60,7 @@ enum flce_status {
   FLCE_ERR_LAUNCH = 5,    /* a kernel launch failed */
   FLCE_ERR_TARGET = 6,    /* (device-side, via *err_flag) target out of range */
   FLCE_ERR_SHAPE = 7,     /* H not a multiple of 8 (bf16) or 4 (fp32) */
-  FLCE_ERR_ALIGN = 8      /* X, W or workspace not 16/16/256-byte aligned, targets not 8 */
+  FLCE_ERR_ALIGN = 8      /* X, W, dX or dW not 16-byte aligned, workspace not 256, targets not 8 */
 };
 
 /* Tokens per chunk that flce_fwd_bwd will use: chunk_tokens if positive
@@ -92,8 +92,9 @@ size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, int64_t chunk_toke
  *            the mean either way.  4-byte aligned.
  *   loss     device float scalar: sum of token losses / N (0 when N == 0)
  *   row_loss [BT] float or NULL: per-token loss l_i (0 on ignored tokens)
- *   dX       [BT, H] dtype: d loss / d X          (may be NULL if BT == 0)
- *   dW       [V, H]  float: d loss / d W, fp32 (overwritten, not accumulated into)
+ *   dX       [BT, H] dtype: d loss / d X, 16-byte aligned (may be NULL if BT == 0)
+ *   dW       [V, H]  float: d loss / d W, fp32 (overwritten, not accumulated into),
+ *            16-byte aligned (the products store 4 consecutive h per lane)
  *   workspace, workspace_bytes: >= flce_workspace_bytes(...), 256-byte aligned
  *   err_flag device int32: 0, or FLCE_ERR_TARGET after the call completes
  * With token_scale NULL the gradients are for an upstream gradient of 1 on the

@@ -80,7 +80,7 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, const flo
   if (BT > 0 && (!X || !targets || !dX)) return FLCE_ERR_ARG;
   if (H % (dtype == FLCE_BF16 ? 8 : 4) != 0) return FLCE_ERR_SHAPE;
   if (!aligned(W, 16) || (X && !aligned(X, 16)) || (targets && !aligned(targets, 8)) || !aligned(workspace, 256) ||
-      !aligned(dW, 4) || (dX && !aligned(dX, dtype == FLCE_BF16 ? 2 : 4)) || (row_loss && !aligned(row_loss, 4)) ||
+      !aligned(dW, 16) || (dX && !aligned(dX, 16)) || (row_loss && !aligned(row_loss, 4)) ||
       (token_scale && !aligned(token_scale, 4)))
     return FLCE_ERR_ALIGN;
   const flce::Layout L = flce::make_layout(BT, H, V, chunk_tokens, dtype);
@@ -185,8 +185,8 @@ int flce_orpo(const void* X, const void* W, const int64_t* targets, int64_t n_se
     return FLCE_ERR_ARG;
   if (!X || !W || !targets || !loss || !dX || !dW || !workspace || !err_flag) return FLCE_ERR_ARG;
   if (H % (dtype == FLCE_BF16 ? 8 : 4) != 0) return FLCE_ERR_SHAPE;
-  if (!aligned(W, 16) || !aligned(X, 16) || !aligned(targets, 8) || !aligned(workspace, 256) || !aligned(dW, 4) ||
-      !aligned(dX, dtype == FLCE_BF16 ? 2 : 4) || (seq_logp && !aligned(seq_logp, 4)))
+  if (!aligned(W, 16) || !aligned(X, 16) || !aligned(targets, 8) || !aligned(workspace, 256) || !aligned(dW, 16) ||
+      !aligned(dX, 16) || (seq_logp && !aligned(seq_logp, 4)))
     return FLCE_ERR_ALIGN;
   const int64_t BT = n_seq * seq_len;
   const OrpoLayout L = orpo_layout(n_seq, seq_len, H, V, chunk_tokens, dtype);

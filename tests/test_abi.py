@@ -100,6 +100,10 @@ def _call(lib, **kw):
         (dict(ws=128), 8),
         (dict(t=20), 8),
         (dict(s=18), 8),
+        # the products store 16-byte (fp32) or 8-byte (bf16) pieces of dX and dW rows
+        (dict(dX=20), 8),
+        (dict(dX=24, dt=BF16, H=128), 8),
+        (dict(dW=20), 8),
         (dict(wsb=16), 3),
     ],
 )
@@ -201,6 +205,8 @@ def _call_orpo(lib, **kw):
         (dict(H=130), 7),
         (dict(X=24), 8),
         (dict(sl=18), 8),
+        (dict(dX=24), 8),
+        (dict(dW=20), 8),
         (dict(ws=128), 8),
         (dict(wsb=16), 3),
     ],
