@@ -59,7 +59,7 @@ enum flce_status {
   FLCE_ERR_DEVICE = 4,    /* current device is not gfx950 */
   FLCE_ERR_LAUNCH = 5,    /* a kernel launch failed */
   FLCE_ERR_TARGET = 6,    /* (device-side, via *err_flag) target out of range */
-  FLCE_ERR_SHAPE = 7,     /* H not a multiple of 8 (bf16) or 4 (fp32) */
+  FLCE_ERR_SHAPE = 7,     /* H not a multiple of 8 (bf16) or 4 (fp32), or a 256-row tile too large (below) */
   FLCE_ERR_ALIGN = 8      /* X, W, dX or dW not 16-byte aligned, workspace not 256, targets not 8 */
 };
 
@@ -98,7 +98,12 @@ size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, int64_t chunk_toke
  *   workspace, workspace_bytes: >= flce_workspace_bytes(...), 256-byte aligned
  *   err_flag device int32: 0, or FLCE_ERR_TARGET after the call completes
  * With token_scale NULL the gradients are for an upstream gradient of 1 on the
- * mean loss; scale them for another. */
+ * mean loss; scale them for another.
+ * Size limits (status FLCE_ERR_SHAPE): the kernels address a 256-row tile with
+ * 32-bit byte offsets, so 256 * H * esize, 256 * round_up(V, 256) * esize and,
+ * for bf16, 256 * round_up(chunk, 64) * 2 must each be below 2^31 (esize 2 for
+ * bf16, 4 for fp32: V up to ~4.19 M for bf16, ~2.09 M for fp32).  flce_fwd
+ * checks only the first; flce_orpo checks all three. */
 int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, const float* token_scale, int64_t BT,
                  int64_t H, int64_t V, int64_t ignore_index, int64_t chunk_tokens, int dtype, float* loss,
                  float* row_loss, void* dX, float* dW, void* workspace, size_t workspace_bytes, int32_t* err_flag,

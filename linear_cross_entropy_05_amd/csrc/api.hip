@@ -39,6 +39,21 @@ int current_device_ok() {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// The kernels address one 256-row tile of an operand, or of the chunk buffer,
+// through a buffer resource with 32-bit byte offsets whose range is capped at
+// 2^31 - 1 bytes: a 256-row tile of W or X ([.., H]), of the chunk buffer
+// ([.., V rounded up to 256]) and of the transposed token chunk ([H, C
+// rounded up to 64], bf16) must fit.  Larger shapes are rejected rather than
+// computed with dropped accesses.
+bool tiles_fit(const flce::Layout& L, bool chunk_buffer) {
+  constexpr int64_t kMax = INT32_MAX;
+  const int64_t rows = 256;
+  if (rows * L.H * L.esize > kMax) return false;
+  if (chunk_buffer && rows * L.ldz * L.esize > kMax) return false;
+  if (chunk_buffer && L.dtype == FLCE_BF16 && rows * L.ldxt * 2 > kMax) return false;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -52,7 +67,9 @@ const char* flce_status_str(int status) {
     case FLCE_ERR_DEVICE: return "current device is not gfx950";
     case FLCE_ERR_LAUNCH: return "kernel launch failed";
     case FLCE_ERR_TARGET: return "target outside [0, V) that is not ignore_index";
-    case FLCE_ERR_SHAPE: return "unsupported shape (H must be a multiple of 8 for bf16, 4 for fp32)";
+    case FLCE_ERR_SHAPE:
+      return "unsupported shape (H must be a multiple of 8 for bf16, 4 for fp32; 256 rows of W, of the logits "
+             "chunk and of the transposed token chunk must each fit in 2^31 bytes)";
     case FLCE_ERR_ALIGN: return "misaligned pointer";
     default: return "unknown status";
   }
@@ -84,6 +101,7 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, const flo
       (token_scale && !aligned(token_scale, 4)))
     return FLCE_ERR_ALIGN;
   const flce::Layout L = flce::make_layout(BT, H, V, chunk_tokens, dtype);
+  if (!tiles_fit(L, true)) return FLCE_ERR_SHAPE;
   if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE;
   if (current_device_ok() != 1) return FLCE_ERR_DEVICE;
 
@@ -124,6 +142,7 @@ int flce_fwd(const void* X, const void* W, const int64_t* targets, int64_t BT, i
       (row_loss && !aligned(row_loss, 4)))
     return FLCE_ERR_ALIGN;
   const flce::Layout L = flce::make_fwd_layout(BT, H, V, chunk_tokens, dtype);
+  if (!tiles_fit(L, false)) return FLCE_ERR_SHAPE;
   if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE;
   if (current_device_ok() != 1) return FLCE_ERR_DEVICE;
 
@@ -190,6 +209,7 @@ int flce_orpo(const void* X, const void* W, const int64_t* targets, int64_t n_se
     return FLCE_ERR_ALIGN;
   const int64_t BT = n_seq * seq_len;
   const OrpoLayout L = orpo_layout(n_seq, seq_len, H, V, chunk_tokens, dtype);
+  if (!tiles_fit(L.fb, true) || !tiles_fit(L.fwd, false)) return FLCE_ERR_SHAPE;
   if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE;
   if (current_device_ok() != 1) return FLCE_ERR_DEVICE;
 

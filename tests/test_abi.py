@@ -105,6 +105,13 @@ def _call(lib, **kw):
         (dict(dX=24, dt=BF16, H=128), 8),
         (dict(dW=20), 8),
         (dict(wsb=16), 3),
+        # a 256-row tile of the logits chunk past 2^31 bytes (V = 4.2 M bf16, 2.1 M fp32)
+        (dict(V=4_200_000, dt=BF16, C=1, wsb=1 << 62), 7),
+        (dict(V=2_100_000, C=1, wsb=1 << 62), 7),
+        # a 256-row tile of W past 2^31 bytes (H = 4.2 M bf16)
+        (dict(H=4_200_000, dt=BF16, C=1, wsb=1 << 62), 7),
+        # the transposed token chunk (bf16 only): chunk of 4.2 M tokens
+        (dict(BT=4_200_000, H=8, dt=BF16, C=4_200_000, wsb=1 << 62), 7),
     ],
 )
 def test_host_argument_checks(lib, kw, status):
@@ -141,6 +148,7 @@ def _call_fwd(lib, **kw):
         (dict(ws=128), 8),
         (dict(t=20), 8),
         (dict(rl=18), 8),
+        (dict(H=4_200_000, dt=BF16, C=1, wsb=1 << 62), 7),
         (dict(wsb=16), 3),
     ],
 )
