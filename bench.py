@@ -92,11 +92,12 @@ def gpu_bench(w, steps, warmup, forward=True):
     wall_ms = (wall1 - wall0) * 1e3 / steps
 
     # forward only (evaluation path), timed separately and reported as context
-    fwd_ms = orpo = eager = None
+    fwd_ms = orpo = eager = lib = None
     if forward:
         fwd_ms = time_forward(flce, w, Xd, Wd, yd, steps, stream, float(out[0].item()))
         orpo = time_orpo(flce, w, Xd, Wd, yd, stream)
         eager = time_torch_eager(w, Xd, Wd, yd, stream, float(out[0].item()))
+        lib = time_library_gemms(w, Xd, Wd, C, stream)
     err = int(out[3].item())
     if err != 0:
         raise RuntimeError(f"device reported error flag {err}")
@@ -107,7 +108,7 @@ def gpu_bench(w, steps, warmup, forward=True):
     log(f"[bench] {ms:.3f} ms/step (wall {wall_ms:.3f}); kernels: "
         + ", ".join(f"{k} {v['ms_per_step']:.3f}" for k, v in kernels.items()))
     return {"ms": ms, "ms_min": per_step[0], "ms_median": per_step[len(per_step) // 2], "fwd_ms": fwd_ms,
-            "orpo": orpo, "eager": eager, "C": C, "ws_bytes": ws_bytes, "peak_extra": peak_extra,
+            "orpo": orpo, "eager": eager, "lib": lib, "C": C, "ws_bytes": ws_bytes, "peak_extra": peak_extra,
             "loss": loss,
             "kernels": kernels,
             "cus": props.multi_processor_count, "arch": getattr(props, "gcnArchName", "?")}
@@ -183,6 +184,46 @@ def time_torch_eager(w, Xd, Wd, yd, stream, loss_flce, reps=3):
     return {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.BT / (ms * 1e-3), 1),
             "peak_extra_bytes": int(peak), "loss": le,
             "what": "torch.mm(X, W.t()) in the input dtype + F.cross_entropy(fp32 logits) + autograd backward"}
+
+
+def time_library_gemms(w, Xd, Wd, C, stream, reps=5):
+    """The three products of one chunk done by the vendor GEMM (torch.mm, i.e.
+    hipBLASLt) on the same shapes (context only): logits X_c W^T, dX = G W and
+    dW = G^T X_c, each with a plain output in the input dtype (no softmax
+    statistics, no fp32 dW read-modify-write).  ms per product and TFLOP/s."""
+    import torch
+
+    if Xd.dtype != torch.bfloat16:
+        return None
+    Xc = Xd[:C]
+    G = torch.mm(Xc, Wd.t())  # [C, V], reused as the gradient operand
+    shapes = {
+        "logits": lambda: torch.mm(Xc, Wd.t()),
+        "dx": lambda: torch.mm(G, Wd),
+        "dw": lambda: torch.mm(G.t(), Xc),
+    }
+    out = {}
+    flops = 2.0 * C * w.H * w.V
+    for name, f in shapes.items():
+        for _ in range(2):
+            r = f()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            r = f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+        del r
+    del G
+    torch.cuda.empty_cache()
+    log("[bench] vendor GEMMs per chunk: " + ", ".join(f"{k} {v['ms']:.3f} ms" for k, v in out.items()))
+    out["what"] = (f"torch.mm (hipBLASLt) on one {C}-token chunk: X_c W^T, G W, G^T X_c, bf16 outputs; "
+                   "this library's products also compute the softmax statistics (logits) and accumulate dW in fp32")
+    return out
 
 
 def time_orpo(flce, w, Xd, Wd, yd, stream, seq_len=1024, reps=3):
@@ -419,6 +460,9 @@ def main(argv=None):
         "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in r["kernels"].items()},
         "orpo": r["orpo"],
         "torch_eager": r["eager"],
+        "vendor_gemm_per_chunk": None if r["lib"] is None else dict(
+            r["lib"], this_library_ms={k: round(r["kernels"][k]["avg_ms"], 4) for k in ("logits", "dx", "dw")
+                                       if k in r["kernels"]}),
         "ce_inplace": ce,
         "forward_only": None if r["fwd_ms"] is None else {
             "ms_per_step": round(r["fwd_ms"], 4), "tokens_per_s": round(w.BT / (r["fwd_ms"] * 1e-3), 1),
