@@ -121,6 +121,30 @@ def _check_tensor(name, t, dtype=None, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
 
 
+def _same_device(dev, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev} (all operands on one device)")
+
+
+def _check_out(name, t, shape, dtype, dev):
+    """A caller-supplied output: the kernels write exactly `shape` elements of `dtype` there."""
+    _check_tensor(name, t, dtype=dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _same_device(dev, **{name: t})
+
+
+def _workspace(workspace, need: int, dev):
+    """The caller's workspace (checked) or a new one of `need` bytes; returns (tensor, bytes)."""
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    else:
+        _check_tensor("workspace", workspace)
+        _same_device(dev, workspace=workspace)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def flce_chunk_tokens(BT: int, H: int, V: int, chunk_tokens: int = 0, dtype=torch.bfloat16) -> int:
     return int(load_library().flce_chunk_tokens(BT, H, V, chunk_tokens, _DTYPES[dtype]))
 
@@ -168,6 +192,7 @@ def flce_fwd_bwd(X, W, targets, ignore_index: int = -100, chunk_tokens: int = 0,
     if W.shape[1] != H or targets.shape[0] != BT:
         raise ValueError(f"shape mismatch X{tuple(X.shape)} W{tuple(W.shape)} targets{tuple(targets.shape)}")
     dev = X.device
+    _same_device(dev, W=W, targets=targets, token_scale=token_scale)
     if out is None:
         loss = torch.empty((), dtype=torch.float32, device=dev)
         dX = torch.empty_like(X)
@@ -175,13 +200,18 @@ def flce_fwd_bwd(X, W, targets, ignore_index: int = -100, chunk_tokens: int = 0,
         err = torch.empty((1,), dtype=torch.int32, device=dev)
     else:
         loss, dX, dW, err = out
+        _check_out("out loss", loss, (), torch.float32, dev)
+        _check_out("out dX", dX, (BT, H), X.dtype, dev)
+        _check_out("out dW", dW, (V, H), torch.float32, dev)
+        _check_out("out err", err, (1,), torch.int32, dev)
     rl = torch.empty((BT,), dtype=torch.float32, device=dev) if row_loss else None
     need = lib.flce_workspace_bytes(BT, H, V, chunk_tokens, _DTYPES[X.dtype])
-    if workspace is None:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
-    st = lib.flce_fwd_bwd(
-        _ptr(X), _ptr(W), _ptr(targets), _ptr(token_scale), BT, H, V, ignore_index, chunk_tokens, _DTYPES[X.dtype],
-        _ptr(loss), _ptr(rl), _ptr(dX), _ptr(dW), _ptr(workspace), workspace.numel(), _ptr(err), _stream(dev))
+    workspace, ws_bytes = _workspace(workspace, need, dev)
+    with torch.cuda.device(dev):
+        st = lib.flce_fwd_bwd(
+            _ptr(X), _ptr(W), _ptr(targets), _ptr(token_scale), BT, H, V, ignore_index, chunk_tokens,
+            _DTYPES[X.dtype], _ptr(loss), _ptr(rl), _ptr(dX), _ptr(dW), _ptr(workspace), ws_bytes, _ptr(err),
+            _stream(dev))
     if st != 0:
         raise FlceError(st, "flce_fwd_bwd")
     if check:
@@ -210,17 +240,20 @@ def flce_forward(X, W, targets, ignore_index: int = -100, chunk_tokens: int = 0,
     if W.shape[1] != H or targets.shape[0] != BT:
         raise ValueError(f"shape mismatch X{tuple(X.shape)} W{tuple(W.shape)} targets{tuple(targets.shape)}")
     dev = X.device
+    _same_device(dev, W=W, targets=targets)
     if out is None:
         loss = torch.empty((), dtype=torch.float32, device=dev)
         err = torch.empty((1,), dtype=torch.int32, device=dev)
     else:
         loss, err = out
+        _check_out("out loss", loss, (), torch.float32, dev)
+        _check_out("out err", err, (1,), torch.int32, dev)
     rl = torch.empty((BT,), dtype=torch.float32, device=dev) if row_loss else None
     need = lib.flce_fwd_workspace_bytes(BT, H, V, chunk_tokens, _DTYPES[X.dtype])
-    if workspace is None:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
-    st = lib.flce_fwd(_ptr(X), _ptr(W), _ptr(targets), BT, H, V, ignore_index, chunk_tokens, _DTYPES[X.dtype],
-                      _ptr(loss), _ptr(rl), _ptr(workspace), workspace.numel(), _ptr(err), _stream(dev))
+    workspace, ws_bytes = _workspace(workspace, need, dev)
+    with torch.cuda.device(dev):
+        st = lib.flce_fwd(_ptr(X), _ptr(W), _ptr(targets), BT, H, V, ignore_index, chunk_tokens, _DTYPES[X.dtype],
+                          _ptr(loss), _ptr(rl), _ptr(workspace), ws_bytes, _ptr(err), _stream(dev))
     if st != 0:
         raise FlceError(st, "flce_fwd")
     if check:
@@ -250,6 +283,7 @@ def flce_orpo(X, W, targets, beta: float = 0.1, ignore_index: int = -100, chunk_
     if X.numel() != n_seq * T * H or X.shape[-1] != H:
         raise ValueError(f"X{tuple(X.shape)} does not match targets{tuple(targets.shape)} and H={H}")
     dev = X.device
+    _same_device(dev, W=W, targets=targets)
     loss = torch.empty((), dtype=torch.float32, device=dev)
     dX = torch.empty_like(X)
     dW = torch.empty((V, H), dtype=torch.float32, device=dev)
@@ -257,9 +291,10 @@ def flce_orpo(X, W, targets, beta: float = 0.1, ignore_index: int = -100, chunk_
     sl = torch.empty((n_seq,), dtype=torch.float32, device=dev) if seq_logp else None
     ws = torch.empty((lib.flce_orpo_workspace_bytes(n_seq, T, H, V, chunk_tokens, _DTYPES[X.dtype]),),
                      dtype=torch.uint8, device=dev)
-    st = lib.flce_orpo(_ptr(X), _ptr(W), _ptr(targets), n_seq, T, H, V, ignore_index, float(beta), chunk_tokens,
-                       _DTYPES[X.dtype], _ptr(loss), _ptr(sl), _ptr(dX), _ptr(dW), _ptr(ws), ws.numel(), _ptr(err),
-                       _stream(dev))
+    with torch.cuda.device(dev):
+        st = lib.flce_orpo(_ptr(X), _ptr(W), _ptr(targets), n_seq, T, H, V, ignore_index, float(beta), chunk_tokens,
+                           _DTYPES[X.dtype], _ptr(loss), _ptr(sl), _ptr(dX), _ptr(dW), _ptr(ws), ws.numel(), _ptr(err),
+                           _stream(dev))
     if st != 0:
         raise FlceError(st, "flce_orpo")
     if check:
@@ -278,12 +313,14 @@ def ce_fwd_bwd_inplace(logits, targets, ignore_index: int = -100, *, row_loss: b
     if targets.shape[0] != BT:
         raise ValueError("targets length must equal logits rows")
     dev = logits.device
+    _same_device(dev, targets=targets)
     loss = torch.empty((), dtype=torch.float32, device=dev)
     err = torch.empty((1,), dtype=torch.int32, device=dev)
     rl = torch.empty((BT,), dtype=torch.float32, device=dev) if row_loss else None
     ws = torch.empty((lib.ce_workspace_bytes(BT, V),), dtype=torch.uint8, device=dev)
-    st = lib.ce_fwd_bwd_inplace(_ptr(logits), _ptr(targets), BT, V, ignore_index, _ptr(loss), _ptr(rl), _ptr(ws),
-                                ws.numel(), _ptr(err), _stream(dev))
+    with torch.cuda.device(dev):
+        st = lib.ce_fwd_bwd_inplace(_ptr(logits), _ptr(targets), BT, V, ignore_index, _ptr(loss), _ptr(rl), _ptr(ws),
+                                    ws.numel(), _ptr(err), _stream(dev))
     if st != 0:
         raise FlceError(st, "ce_fwd_bwd_inplace")
     if check:
