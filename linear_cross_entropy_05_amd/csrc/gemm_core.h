@@ -365,6 +365,10 @@ __device__ __forceinline__ u32x4 rsrc_words(const void* base, int64_t bytes) {
 // pipeline places the waits itself (wait_vm), also in inline asm.  The
 // bounds check of a raw buffer covers the VGPR offset, so every offset that
 // can leave the operand lives there; the scalar offset only carries k0.
+// m0 (the LDS destination) is set inside the same asm statement, so nothing
+// here relies on it surviving; hipcc warns that it may not preserve a
+// clobbered m0 for its own code, and the kernels' generated code writes and
+// reads m0 only in these statements.
 __device__ __forceinline__ void dma16(u32x4 r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
