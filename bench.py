@@ -394,9 +394,20 @@ def cpu_baseline(w, sample_tokens):
         ref = oracle.flce_ref(Xs, W, ys, w.ignore_index)
         dt = time.perf_counter() - t0
     log(f"[bench] cpu oracle {dt:.2f} s (loss on sample {ref['loss']:.5f})")
+    import resource
+
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    rss_gb = resource.getrusage(resource.RUSAGE_SELF).ru_maxrss / 2**20  # KiB -> GiB
     return {"value": round(S / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"first {S} of {w.BT} tokens of the {w.name} workload with the full W "
-                      f"[{w.V}, {w.H}]; NumPy float64 fwd+bwd, {dt:.2f} s"}
+                      f"[{w.V}, {w.H}]; NumPy float64 fwd+bwd, {dt:.2f} s",
+            "cpu_model": model, "blas": blas[0].get("internal_api") if blas else None,
+            "peak_rss_gib": round(rss_gb, 1)}
 
 
 def main(argv=None):
