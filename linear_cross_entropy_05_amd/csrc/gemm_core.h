@@ -679,7 +679,8 @@ __device__ __forceinline__ void mainloop_kc_reg(char* smem, const Operand<__bf16
 #pragma unroll
     for (int q = 0; q < kLoads; ++q) sb[q] = ld(rsb, lb, b1, q);
   }
-  __syncthreads();  // stage 0 is in LDS
+  // stage 0 is in LDS (its writes waited for their loads); stage 1 stays in flight
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 
   u32x4 fa[2][4], fb[2][4];
   load_frags<false>(la, smem, 0, wy, lane, fa[0]);
