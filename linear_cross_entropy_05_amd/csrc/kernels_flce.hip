@@ -171,13 +171,18 @@ __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
     // logit they add exp(kPad - m) = 0 to a block's sum; a block with no
     // entry below V gets (M_h, s_h) = (kPad, 0), which the lse combine
     // weighs by exp(M_h - M) = 0, and the gradient pass zeroes those columns.
+    // This lane's entries sit at vw + a compile-time offset (< 128), so one
+    // 32-bit count of valid entries from vw decides them all.
+    const int nvalid_v = (int)(a.V - vw < 128 ? a.V - vw : 128);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int e = 0; e < 16; ++e) {
+        const bool pad = 32 * i + 8 * (e >> 2) + (e & 3) >= nvalid_v;
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (vw + 32 * i + 8 * (e >> 2) + (e & 3) >= a.V) acc[i][j][e] = kPad;
+        for (int j = 0; j < 4; ++j)
+          if (pad) acc[i][j][e] = kPad;
+      }
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
