@@ -426,7 +426,7 @@ def main(argv=None):
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     a = ap.parse_args(argv)
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); this library has no multi-GPU path.",
               file=sys.stderr)
         return 2
 

@@ -35,7 +35,7 @@ float64 with the full BT x V logits materialised:
     G_iv   = (exp(Z_iv - lse_i) - [v == y_i]) / N  (0 for ignored rows)
     dX     = G W,   dW = G^T X
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 the reduction is the mean over non-ignored tokens of the whole call; no bias
 term (the usage example passes only ``model.weight``); N = 0 gives loss 0 and
 zero gradients; a valid target outside [0, V) is an error, never clamped;
