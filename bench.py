@@ -72,24 +72,36 @@ def gpu_bench(w, steps, warmup, forward=True):
     torch.cuda.synchronize()
     log(f"[bench] warmup {warmup} done; timing {steps} steps")
 
+    # the headline: K whole calls with nothing else on the stream between them
     stream = torch.cuda.current_stream(dev)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    with flce.KernelTimer(max_launches=64 * steps + 64) as kt:
-        torch.cuda.synchronize()
-        wall0 = time.perf_counter()
-        t0.record(stream)
-        marks[0].record(stream)
-        for i in range(steps):
-            flce.flce_fwd_bwd(Xd, Wd, yd, w.ignore_index, w.chunk_tokens, out=out, workspace=workspace, check=False)
-            marks[i + 1].record(stream)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        wall1 = time.perf_counter()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    marks[0].record(stream)
+    for i in range(steps):
+        flce.flce_fwd_bwd(Xd, Wd, yd, w.ignore_index, w.chunk_tokens, out=out, workspace=workspace, check=False)
+        marks[i + 1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall1 = time.perf_counter()
     ms = t0.elapsed_time(t1) / steps
     per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
     wall_ms = (wall1 - wall0) * 1e3 / steps
+
+    # per-kernel times from a second loop of K calls with the library's event
+    # hooks on (two event records around every launch, on its stream)
+    with flce.KernelTimer(max_launches=64 * steps + 64) as kt:
+        h0 = torch.cuda.Event(enable_timing=True)
+        h1 = torch.cuda.Event(enable_timing=True)
+        h0.record(stream)
+        for i in range(steps):
+            flce.flce_fwd_bwd(Xd, Wd, yd, w.ignore_index, w.chunk_tokens, out=out, workspace=workspace, check=False)
+        h1.record(stream)
+        torch.cuda.synchronize()
+    hooked_ms = h0.elapsed_time(h1) / steps
 
     # forward only (evaluation path), timed separately and reported as context
     fwd_ms = orpo = eager = lib = None
@@ -105,9 +117,10 @@ def gpu_bench(w, steps, warmup, forward=True):
     kernels = {k: {"avg_ms": kt.ms[k] / kt.launches[k], "launches_per_step": kt.launches[k] / steps,
                    "ms_per_step": kt.ms[k] / steps}
                for k in kt.ms if kt.launches[k]}
-    log(f"[bench] {ms:.3f} ms/step (wall {wall_ms:.3f}); kernels: "
+    log(f"[bench] {ms:.3f} ms/step (wall {wall_ms:.3f}); with kernel hooks {hooked_ms:.3f}; kernels: "
         + ", ".join(f"{k} {v['ms_per_step']:.3f}" for k, v in kernels.items()))
     return {"ms": ms, "ms_min": per_step[0], "ms_median": per_step[len(per_step) // 2], "fwd_ms": fwd_ms,
+            "hooked_ms": hooked_ms,
             "orpo": orpo, "eager": eager, "lib": lib, "C": C, "ws_bytes": ws_bytes, "peak_extra": peak_extra,
             "loss": loss,
             "kernels": kernels,
@@ -469,6 +482,8 @@ def main(argv=None):
         "roofline": roof,
         "mfma_counters": measured_mfma(dom, roof["achieved"] if roof["unit"] == "TFLOP/s" else None),
         "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in r["kernels"].items()},
+        "kernels_sum_ms_per_step": round(sum(v["ms_per_step"] for v in r["kernels"].values()), 4),
+        "kernels_loop_ms_per_step": round(r["hooked_ms"], 4),
         "orpo": r["orpo"],
         "torch_eager": r["eager"],
         "vendor_gemm_per_chunk": None if r["lib"] is None else dict(

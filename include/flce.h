@@ -26,8 +26,14 @@
  *
  * Conventions for every entry point.
  *   - All array pointers are DEVICE pointers owned by the caller; the library
- *     allocates nothing and keeps no state between calls (apart from a
- *     per-device "is this a gfx950" answer).  Row-major, densely packed.
+ *     allocates nothing.  Row-major, densely packed.
+ *   - Process-global state: a per-device "is this a gfx950" answer (filled
+ *     on first use, safe to fill from several threads), and the optional
+ *     kernel-timing switch of flce_profile_begin / flce_profile_end (not
+ *     thread-safe; while it is on, every launch from any thread records
+ *     events into one shared table).  Nothing else persists between calls.
+ *   - Sizes (tokens, hidden size, vocabulary) must be below 2^31; larger
+ *     ones return FLCE_ERR_ARG (queries return 0).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream).  Results are valid once the stream has been synchronised.
  *   - Problems detectable on the host are reported by the return value
@@ -53,7 +59,7 @@ enum flce_dtype { FLCE_F32 = 0, FLCE_BF16 = 1 };
 /* Status codes. */
 enum flce_status {
   FLCE_OK = 0,
-  FLCE_ERR_ARG = 1,       /* null pointer, negative or zero size */
+  FLCE_ERR_ARG = 1,       /* null pointer, negative, zero or >= 2^31 size */
   FLCE_ERR_DTYPE = 2,     /* dtype not one of flce_dtype */
   FLCE_ERR_WORKSPACE = 3, /* workspace_bytes below what *_workspace_bytes returns */
   FLCE_ERR_DEVICE = 4,    /* current device is not gfx950 */

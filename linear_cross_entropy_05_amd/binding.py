@@ -20,7 +20,7 @@ import re
 import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.environ.get("FLCE_LIB") or os.path.join(PKG, "libflce.so")
+LIB_PATH = os.path.join(PKG, "libflce.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "flce.h")
 
 FLCE_F32, FLCE_BF16 = 0, 1

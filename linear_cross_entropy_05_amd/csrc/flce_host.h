@@ -1,0 +1,71 @@
+// Host side of the C-ABI entry points that touches no device: argument
+// checks, the chunk rule and the workspace layouts.  Plain C++ with no HIP
+// header, so the same unit is compiled into libflce and, with the address and
+// undefined-behaviour sanitizers, into a CPU test program.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace flce {
+
+constexpr int kTile = 256;      // output tile edge (M and N) of the MFMA products
+constexpr int kRowBytes = 128;  // K bytes per tile row per pipeline stage
+
+// Workspace of one flce_fwd_bwd call: where each scratch array lives.  The
+// chunk buffer holds one chunk's logits, then (in place) their gradient; it
+// is the only large array.  Offsets are in bytes from the workspace base,
+// each 256-byte aligned.
+struct Layout {
+  int64_t BT, H, V;
+  int dtype;        // 0 fp32, 1 bf16
+  int64_t C;        // tokens per chunk
+  int64_t ldz;      // elements between chunk rows (V rounded up to 256)
+  int64_t nvt;      // vocabulary tiles of the logits GEMM (ceil(V / 256)); statistics per half tile
+  int64_t splits;   // K splits of the dX GEMM
+  int64_t esize;    // bytes per element of X, W and the chunk
+  int64_t ldxt;     // bf16: elements between rows of the transposed token chunk X_c^T [H, ldxt]
+  // X_c^T shares the statistics region (off_part): the statistics are dead
+  // once the gradient pass has run, and X_c^T is only read by the dW product
+  size_t off_nvalid, off_lse, off_rowloss, off_part, off_chunk, off_dxpart, total;
+};
+
+Layout make_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);
+// Forward only: no chunk buffer; off_chunk == off_dxpart == total.
+Layout make_fwd_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);
+
+// Workspace of flce_orpo: per-token arrays and per-sequence sums, then one
+// region that the forward-only pass and then the fused pass reuse.
+struct OrpoLayout {
+  size_t off_nvalid, off_rowloss, off_scale, off_scratch, off_region, total;
+  Layout fwd, fb;
+};
+OrpoLayout make_orpo_layout(int64_t n_seq, int64_t seq_len, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);
+
+// Bytes of the logits-only cross-entropy workspace: the valid-token count
+// and, when the caller passes no row_loss, BT floats of token losses.
+size_t ce_layout_bytes(int64_t BT);
+
+// The kernels address one 256-row tile of an operand (or of the chunk
+// buffer, or of the transposed token chunk) through 32-bit byte offsets
+// below 2^31: false if a tile of these sizes would not fit.
+bool tiles_fit(const Layout& L, bool chunk_buffer);
+
+// Checks an entry point makes before it touches a device.  Each returns
+// FLCE_OK or the status the entry point returns (flce_status in flce.h),
+// and, on FLCE_OK, the layout the call will use.
+int check_fwd_bwd(const void* X, const void* W, const int64_t* targets, const float* token_scale, int64_t BT,
+                  int64_t H, int64_t V, int64_t chunk_tokens, int dtype, const float* loss, const float* row_loss,
+                  const void* dX, const float* dW, const void* workspace, size_t workspace_bytes,
+                  const int32_t* err_flag, Layout* L);
+int check_fwd(const void* X, const void* W, const int64_t* targets, int64_t BT, int64_t H, int64_t V,
+              int64_t chunk_tokens, int dtype, const float* loss, const float* row_loss, const void* workspace,
+              size_t workspace_bytes, const int32_t* err_flag, Layout* L);
+int check_orpo(const void* X, const void* W, const int64_t* targets, int64_t n_seq, int64_t seq_len, int64_t H,
+               int64_t V, int64_t chunk_tokens, int dtype, const float* loss, const float* seq_logp, const void* dX,
+               const float* dW, const void* workspace, size_t workspace_bytes, const int32_t* err_flag,
+               OrpoLayout* L);
+int check_ce(const float* logits, const int64_t* targets, int64_t BT, int64_t V, const float* loss,
+             const float* row_loss, const void* workspace, size_t workspace_bytes, const int32_t* err_flag);
+
+}  // namespace flce

@@ -5,29 +5,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "flce_host.h"
+
 namespace flce {
-
-// Workspace of one flce_fwd_bwd call: where each scratch array lives.  The
-// chunk buffer holds one chunk's logits, then (in place) their gradient; it
-// is the only large array.  Offsets are in bytes from the workspace base,
-// each 256-byte aligned.
-struct Layout {
-  int64_t BT, H, V;
-  int dtype;        // 0 fp32, 1 bf16
-  int64_t C;        // tokens per chunk
-  int64_t ldz;      // elements between chunk rows (V rounded up to 256)
-  int64_t nvt;      // vocabulary tiles of the logits GEMM (ceil(V / 256)); statistics per half tile
-  int64_t splits;   // K splits of the dX GEMM
-  int64_t esize;    // bytes per element of X, W and the chunk
-  int64_t ldxt;     // bf16: elements between rows of the transposed token chunk X_c^T [H, ldxt]
-  // X_c^T shares the statistics region (off_part): the statistics are dead
-  // once the gradient pass has run, and X_c^T is only read by the dW product
-  size_t off_nvalid, off_lse, off_rowloss, off_part, off_chunk, off_dxpart, total;
-};
-
-Layout make_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);
-// Forward only: no chunk buffer; off_chunk == off_dxpart == total.
-Layout make_fwd_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);
 
 // Kernel kinds, in the order flce_profile_end reports them.
 enum Phase {

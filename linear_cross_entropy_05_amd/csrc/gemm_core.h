@@ -35,6 +35,8 @@
 
 #include <type_traits>
 
+#include "flce_host.h"
+
 namespace flce {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -44,9 +46,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kTile = 256;                      // output tile edge (M and N)
 constexpr int kThreads = 256;                   // 4 waves
-constexpr int kRowBytes = 128;                  // K bytes per tile row per stage
 constexpr int kOpBytes = kTile * kRowBytes;     // one operand, one stage: 32 KiB
 constexpr int kStageBytes = 2 * kOpBytes;       // A + B
 constexpr int kLdsBytes = 2 * kStageBytes;      // double buffered: 128 KiB
@@ -618,146 +618,6 @@ __device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, i
   __syncthreads();  // the slabs are free for the caller
 }
 
-// Alternative main loop, compiled only with FLCE_KC_REG=1 (not the default):
-// measured 9-10% slower than the ring above on the Llama-3 logits product
-// (3.6 vs 3.3 ms per 4096-token chunk), although a plain copy loop moves
-// L2 -> LDS data ~1.6x faster through VGPRs than with direct-to-LDS copies.
-// Both operands K-contiguous, copies staged through registers: each lane
-// loads its 16-byte pieces of a stage with buffer loads into VGPRs and
-// writes them to the same LDS places the direct copies fill (tile + 1 KiB
-// wave + 4 KiB copy + 16 B lane).  Two stages of LDS (A(b) in slab 2 b, B(b)
-// in slab 2 b + 1, b = stage mod 2).  During stage k, steps 0 (A) and 1 (B),
-// one copy per two MFMAs: copy q of stage k + 1 (loaded during stage k - 1)
-// goes to LDS and its registers at once load copy q of stage k + 2, so every
-// load has a whole stage to land.  The barrier before step 3 (after the LDS
-// writes are done) publishes stage k + 1, whose first fragments step 3 reads.
-__device__ __forceinline__ void mainloop_kc_reg(char* smem, const Operand<__bf16>& A, int64_t m0,
-                                                const Operand<__bf16>& B, int64_t n0, int64_t k0, int64_t k1,
-                                                f32x16 (&acc)[4][4]) {
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wy = wave >> 1, wx = wave & 1;
-  KcLoader la, lb;
-  la.init(A, m0, wave, lane);
-  lb.init(B, n0, wave, lane);
-  const int64_t ra_rows = A.rows - m0 < kTile ? A.rows - m0 : kTile;
-  const int64_t rb_rows = B.rows - n0 < kTile ? B.rows - n0 : kTile;
-  const Rsrc rsa = make_rsrc(A.base + m0 * A.ld, ra_rows * A.ld * 2);
-  const Rsrc rsb = make_rsrc(B.base + n0 * B.ld, rb_rows * B.ld * 2);
-  int nk = (int)((k1 - k0 + kBK - 1) / kBK);
-  if (nk < 0) nk = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-  if (nk <= 0) return;
-  const uint32_t wofs = 1024u * (uint32_t)wave + 16u * (uint32_t)lane;
-  auto ld = [&](const Rsrc& r, const KcLoader& l, const KcLoader::Stage& st, int q) {
-    return bload16(r, st.in ? l.voff[q] : 0x80000000u, st.soff);
-  };
-  auto wr = [&](char* tile, int q, const u32x4& v) { *reinterpret_cast<u32x4*>(tile + wofs + 4096u * q) = v; };
-
-  u32x4 sa[kLoads], sb[kLoads];
-  {
-    const auto a0 = la.stage(k0, true);
-    const auto b0 = lb.stage(k0, true);
-#pragma unroll
-    for (int q = 0; q < kLoads; ++q) {
-      sa[q] = ld(rsa, la, a0, q);
-      sb[q] = ld(rsb, lb, b0, q);
-    }
-#pragma unroll
-    for (int q = 0; q < kLoads; ++q) {
-      wr(smem, q, sa[q]);
-      wr(smem + kSlab, q, sb[q]);
-    }
-    // stage 1 in the order the loop reloads the registers (A, then B), so
-    // the waits for them are the same on entry as in every iteration
-    const auto a1 = la.stage(k0 + kBK, nk > 1);
-    const auto b1 = lb.stage(k0 + kBK, nk > 1);
-#pragma unroll
-    for (int q = 0; q < kLoads; ++q) sa[q] = ld(rsa, la, a1, q);
-#pragma unroll
-    for (int q = 0; q < kLoads; ++q) sb[q] = ld(rsb, lb, b1, q);
-  }
-  // stage 0 is in LDS (its writes waited for their loads); stage 1 stays in flight
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
-
-  u32x4 fa[2][4], fb[2][4];
-  load_frags<false>(la, smem, 0, wy, lane, fa[0]);
-  load_frags<false>(lb, smem + kSlab, 0, wx, lane, fb[0]);
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    const int cur = kt & 1, nxt = cur ^ 1;
-    const char* ta = smem + (2 * cur) * kSlab;
-    const char* tb = smem + (2 * cur + 1) * kSlab;
-    char* wa = smem + (2 * nxt) * kSlab;
-    char* wb = smem + (2 * nxt + 1) * kSlab;
-    const bool more = kt + 2 < nk;
-    const int64_t kn = k0 + (int64_t)(kt + 2) * kBK;
-    const auto sta = la.stage(kn, more);
-    const auto stb = lb.stage(kn, more);
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      load_frags<false>(la, ta, s + 1, wy, lane, fa[(s + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        if (u == 8) {
-          __builtin_amdgcn_sched_barrier(0);
-          load_frags<false>(lb, tb, s + 1, wx, lane, fb[(s + 1) & 1]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        acc[u >> 2][u & 3] = mma_chunk<__bf16>(fa[s & 1][u >> 2], fb[s & 1][u & 3], acc[u >> 2][u & 3]);
-        __builtin_amdgcn_sched_barrier(0);
-#ifndef FLCE_KC_REG_SPREAD
-#define FLCE_KC_REG_SPREAD 3  // one copy per this many MFMAs (3 measured ~1% faster than 2)
-#endif
-        // copy p of stage kt + 1 to LDS, then the same registers load copy p
-        // of stage kt + 2 (p < 8: A, else B)
-        constexpr int kSp = FLCE_KC_REG_SPREAD;
-        const int g = 16 * s + u;
-        if (g % kSp == kSp - 1 && g / kSp < 2 * kLoads) {
-          const int p = g / kSp;
-          if (p < kLoads) {
-            wr(wa, p, sa[p]);
-            sa[p] = ld(rsa, la, sta, p);
-          } else {
-            wr(wb, p - kLoads, sb[p - kLoads]);
-            sb[p - kLoads] = ld(rsb, lb, stb, p - kLoads);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // stage kt + 1 written (LDS writes done) and stage kt's fragments all read
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
-    load_frags<false>(la, wa, 0, wy, lane, fa[0]);
-    load_frags<false>(lb, wb, 0, wx, lane, fb[0]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < 16; ++u)
-      acc[u >> 2][u & 3] = mma_chunk<__bf16>(fa[1][u >> 2], fb[1][u & 3], acc[u >> 2][u & 3]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  {
-    const int cur = (nk - 1) & 1;
-    const char* ta = smem + (2 * cur) * kSlab;
-    const char* tb = smem + (2 * cur + 1) * kSlab;
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      load_frags<false>(la, ta, s + 1, wy, lane, fa[(s + 1) & 1]);
-      load_frags<false>(lb, tb, s + 1, wx, lane, fb[(s + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        acc[u >> 2][u & 3] = mma_chunk<__bf16>(fa[s & 1][u >> 2], fb[s & 1][u & 3], acc[u >> 2][u & 3]);
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u)
-      acc[u >> 2][u & 3] = mma_chunk<__bf16>(fa[1][u >> 2], fb[1][u & 3], acc[u >> 2][u & 3]);
-  }
-  __syncthreads();  // the slabs are free for the caller; no loads are in flight
-}
-
 }  // namespace pipe
 
 // acc = A[m0:m0+256, k0:k1) * B[n0:n0+256, k0:k1)^T: the direct-to-LDS
@@ -766,20 +626,12 @@ static_assert(kLdsBytes <= pipe::kRingBytes, "LDS");
 constexpr int kGemmLdsBytes = pipe::kRingBytes;
 
 // Tile-order group size (consecutive tile rows walked column by column).
-#ifndef FLCE_TILE_GROUP
-#define FLCE_TILE_GROUP 8
-#endif
-constexpr int kTileGroup = FLCE_TILE_GROUP;
+constexpr int kTileGroup = 8;
 
 template <typename T, bool kAKMajor, bool kBKMajor>
 __device__ __forceinline__ void gemm_mainloop(char* smem, const Operand<T>& A, int64_t m0, const Operand<T>& B,
                                               int64_t n0, int64_t k0, int64_t k1, f32x16 (&acc)[4][4]) {
-#ifndef FLCE_KC_REG
-#define FLCE_KC_REG 0  // 1: the register-staged loop for two K-contiguous operands (logits)
-#endif
-  if constexpr (sizeof(T) == 2 && FLCE_KC_REG && !kAKMajor && !kBKMajor)
-    pipe::mainloop_kc_reg(smem, A, m0, B, n0, k0, k1, acc);
-  else if constexpr (sizeof(T) == 2)
+  if constexpr (sizeof(T) == 2)
     pipe::mainloop<kAKMajor, kBKMajor>(smem, A, m0, B, n0, k0, k1, acc);
   else
     mainloop_regstage<T, kAKMajor, kBKMajor>(smem, A, m0, B, n0, k0, k1, acc);

@@ -26,21 +26,14 @@
 #include "flce_internal.h"
 #include "gemm_core.h"
 
-#ifndef FLCE_GRAD_THREADS
-#define FLCE_GRAD_THREADS 1024
-#endif
-#ifndef FLCE_GRAD_UNROLL
-#define FLCE_GRAD_UNROLL 4
-#endif
-
 namespace flce {
 
 constexpr float kLog2e = 1.4426950408889634f;
 // gradient pass: threads per token row and 16-byte loads in flight per
 // thread (1024 x 4 measured ~8% faster than 256 x 4 on 250 KiB rows; 2 and 4
 // loads in flight tie, 8 is slower)
-constexpr int kGradThreads = FLCE_GRAD_THREADS;
-constexpr int kGradUnroll = FLCE_GRAD_UNROLL;
+constexpr int kGradThreads = 1024;
+constexpr int kGradUnroll = 4;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -598,115 +591,6 @@ __global__ __launch_bounds__(1024) void k_loss_final(const float* __restrict__ r
 }
 
 // ---- host side ------------------------------------------------------------------------
-
-static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-static int64_t pick_splits(int64_t tiles, int64_t kstages, size_t part_bytes_per_split, size_t chunk_bytes) {
-  // fewest K splits that fill the 256 CUs best, each split keeping >= 16
-  // stages of K, the fp32 partials within half the chunk buffer or 128 MiB,
-  // whichever is larger (small chunks would otherwise leave most CUs idle)
-  constexpr int64_t kCUs = 256;
-  const size_t cap = chunk_bytes / 2 > ((size_t)128 << 20) ? chunk_bytes / 2 : ((size_t)128 << 20);
-  int64_t best = 1;
-  double best_cost = (double)((tiles + kCUs - 1) / kCUs);
-  for (int64_t s = 2; s <= 16; ++s) {
-    if (kstages / s < 16) break;
-    if ((size_t)s * part_bytes_per_split > cap) break;
-    const double cost = (double)((tiles * s + kCUs - 1) / kCUs) / (double)s;
-    if (cost < best_cost * 0.97) {
-      best = s;
-      best_cost = cost;
-    }
-  }
-  return best;
-}
-
-Layout make_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype) {
-  Layout L{};
-  L.BT = BT;
-  L.H = H;
-  L.V = V;
-  L.dtype = dtype;
-  L.esize = dtype == 1 ? 2 : 4;
-  L.ldz = (V + kTile - 1) / kTile * kTile;
-  L.nvt = (V + kTile - 1) / kTile;
-  int64_t C = chunk_tokens;
-  if (C <= 0) {
-    // as few chunks as keep the chunk buffer within 1 GiB, of equal size
-    // rounded up to whole 256-token tiles (each chunk after the first costs
-    // a read-modify-write of the fp32 dW)
-    const int64_t cmax = ((int64_t)1 << 30) / (L.ldz * L.esize);
-    if (cmax < kTile || BT <= cmax) {
-      C = cmax < 1 ? 1 : cmax;
-    } else {
-      const int64_t nch = (BT + cmax - 1) / cmax;
-      C = ((BT + nch - 1) / nch + kTile - 1) / kTile * kTile;
-      const int64_t cmax_tiles = cmax / kTile * kTile;
-      if (C > cmax_tiles) C = cmax_tiles;
-    }
-  }
-  if (C > BT) C = BT;
-  if (C < 1) C = 1;
-  L.C = C;
-  const int64_t ks = kRowBytes / L.esize;
-  const int64_t tiles = ((C + kTile - 1) / kTile) * ((H + kTile - 1) / kTile);
-  const size_t chunk_bytes = (size_t)C * L.ldz * L.esize;
-  L.splits = pick_splits(tiles, (V + ks - 1) / ks, (size_t)C * H * 4, chunk_bytes);
-  size_t o = 0;
-  L.off_nvalid = o;
-  o = align256(o + 16);
-  L.off_lse = o;
-  o = align256(o + (size_t)C * 4);
-  L.off_rowloss = o;
-  o = align256(o + (size_t)(BT > 0 ? BT : 1) * 4);
-  L.off_part = o;
-  L.ldxt = (C + 63) / 64 * 64;
-  {
-    const size_t stats = (size_t)C * 2 * L.nvt * 8;
-    const size_t xt = dtype == 1 ? (size_t)H * L.ldxt * 2 : 0;
-    o = align256(o + (stats > xt ? stats : xt));
-  }
-  L.off_chunk = o;
-  o = align256(o + chunk_bytes);
-  L.off_dxpart = o;
-  if (L.splits > 1) o = align256(o + (size_t)L.splits * C * H * 4);
-  L.total = o;
-  return L;
-}
-
-Layout make_fwd_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype) {
-  Layout L{};
-  L.BT = BT;
-  L.H = H;
-  L.V = V;
-  L.dtype = dtype;
-  L.esize = dtype == 1 ? 2 : 4;
-  L.ldz = (V + kTile - 1) / kTile * kTile;
-  L.nvt = (V + kTile - 1) / kTile;
-  int64_t C = chunk_tokens;
-  if (C <= 0) {
-    // no logits are kept: a pass is bounded only by its statistics
-    // (8 bytes per token and half tile), at most 256 MiB
-    C = ((int64_t)1 << 28) / (2 * L.nvt * 8);
-  }
-  if (C > BT) C = BT;
-  if (C < 1) C = 1;
-  L.C = C;
-  L.splits = 1;
-  size_t o = 0;
-  L.off_nvalid = o;
-  o = align256(o + 16);
-  L.off_lse = o;
-  o = align256(o + (size_t)C * 4);
-  L.off_rowloss = o;
-  o = align256(o + (size_t)(BT > 0 ? BT : 1) * 4);
-  L.off_part = o;
-  o = align256(o + (size_t)C * 2 * L.nvt * 8);
-  L.off_chunk = o;
-  L.off_dxpart = o;
-  L.total = o;
-  return L;
-}
 
 hipError_t launch_count_valid(const int64_t* y, int64_t BT, int64_t V, int64_t ign, int32_t* nvalid, int32_t* err,
                               hipStream_t s) {

@@ -8,7 +8,8 @@
 //   loss = (sum of chosen token losses) / N_chosen + beta / B * sum_p softplus(-r_p)
 // and the per-token gradient factors w_i = d loss / d l_i that the fused
 // linear + cross-entropy pass then applies to (softmax - onehot).  A pair with
-// a sequence that has no valid token adds nothing to the odds-ratio term.
+// a sequence that has no valid token adds nothing to the odds-ratio term; in
+// that term each a_s is held at or below -2^-24 (see kMaxSeqLogp).
 #include "flce_internal.h"
 
 namespace flce {
@@ -35,6 +36,14 @@ __device__ double block_sum(double v, double* red) {
   for (int k = 0; k < kOrpoWaves; ++k) t += red[k];
   return t;
 }
+
+// The mean log-probability a of a sequence is negative in exact arithmetic,
+// but the fp32 token losses of a near-certain sequence can round to 0 or just
+// below it, which would make log(1 - e^a) infinite or NaN.  The odds-ratio
+// term takes a at most -2^-24: its loss and gradient factors tend to finite
+// limits as a -> 0 (softplus(-r) -> 0, sigmoid(-r) / (1 - e^{a_w}) stays
+// bounded), so the bound changes them only below the fp32 resolution.
+constexpr double kMaxSeqLogp = -0x1p-24;
 
 __device__ __forceinline__ double softplus(double x) { return fmax(x, 0.0) + log1p(exp(-fabs(x))); }
 __device__ __forceinline__ double sigmoid(double x) {
@@ -91,7 +100,7 @@ __global__ __launch_bounds__(kOrpoThreads) void k_orpo_stats(const float* __rest
     const int64_t sw = p, sl = B + p;
     const double nw = scnt[sw], nl = scnt[sl];
     if (nw > 0.0 && nl > 0.0) {
-      const double aw = -ssum[sw] / nw, al = -ssum[sl] / nl;
+      const double aw = fmin(-ssum[sw] / nw, kMaxSeqLogp), al = fmin(-ssum[sl] / nl, kMaxSeqLogp);
       const double ow = -expm1(aw), ol = -expm1(al);  // 1 - e^a
       const double r = (aw - al) - (log(ow) - log(ol));
       orsum += softplus(-r);

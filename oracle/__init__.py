@@ -5,8 +5,8 @@ from .flce_oracle import (  # noqa: F401
     check_targets,
     flce_brute_force,
     flce_ref,
+    flce_ref_rowblocks,
     flce_rows_ref,
     row_lse,
-    valid_rows,
 )
 from .orpo_oracle import orpo_loss_only, orpo_ref, orpo_terms  # noqa: F401,E402

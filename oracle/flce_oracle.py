@@ -67,11 +67,6 @@ def _as_i64(a) -> np.ndarray:
     return np.asarray(a, dtype=np.int64)
 
 
-def valid_rows(y, ignore_index: int = -100) -> np.ndarray:
-    """Boolean mask of rows that contribute to the loss (target != ignore_index)."""
-    return _as_i64(y) != ignore_index
-
-
 def check_targets(y, V: int, ignore_index: int = -100) -> None:
     """Raise ValueError if a non-ignored target lies outside [0, V)."""
     y = _as_i64(y)
@@ -171,6 +166,41 @@ def flce_ref(X, W, y, ignore_index: int = -100, token_scale=None):
     out["dX"] = G @ W64
     out["dW"] = G.T @ X64
     return out
+
+
+def flce_ref_rowblocks(X, W, y, ignore_index: int = -100, block: int = 1024):
+    """``flce_ref`` for hosts without room for the whole BT x V logits.
+
+    The same definition with the token axis cut into blocks of ``block``
+    rows: each row's loss term and gradient row depend only on that row and
+    on the batch's N, so block b's logits Z_b = X_b W^T, its gradient rows
+    G_b and dX_b = G_b W are exactly those rows of the whole computation;
+    dW = G^T X is the sum over blocks of G_b^T X_b (the product's sum over
+    tokens, split).  Returns ``loss``, ``dX``, ``dW``, ``row_loss``, ``lse``
+    and ``n_valid`` (no ``dlogits``), all float64.
+    """
+    X64 = _as_f64(X)
+    W64 = _as_f64(W)
+    y = _as_i64(y)
+    if X64.ndim != 2 or W64.ndim != 2 or X64.shape[1] != W64.shape[1]:
+        raise ValueError(f"shape mismatch X{X64.shape} W{W64.shape}")
+    BT = X64.shape[0]
+    check_targets(y, W64.shape[0], ignore_index)
+    n = int((y != ignore_index).sum())
+    dX = np.zeros_like(X64)
+    dW = np.zeros_like(W64)
+    row_loss = np.zeros(BT)
+    lse = np.zeros(BT)
+    for b in range(0, BT, block):
+        e = min(b + block, BT)
+        out = _ce(X64[b:e] @ W64.T, y[b:e], ignore_index, n_valid=n)
+        G = out["dlogits"]
+        dX[b:e] = G @ W64
+        dW += G.T @ X64[b:e]
+        row_loss[b:e] = out["row_loss"]
+        lse[b:e] = out["lse"]
+    loss = float(row_loss.sum() / max(n, 1))
+    return {"loss": loss, "dX": dX, "dW": dW, "row_loss": row_loss, "lse": lse, "n_valid": n}
 
 
 def flce_rows_ref(X, W, y, rows, n_valid: int, ignore_index: int = -100):

@@ -1,0 +1,124 @@
+// CPU driver for the library's host-only unit (host_checks.cpp), built with
+// the address and undefined-behaviour sanitizers by test_host_sanitize.py.
+//
+// Reads one case per line on stdin and prints one result line per case:
+//   fwd_bwd X W t s BT H V C dt loss rl dX dW ws wsb err  -> status of check_fwd_bwd
+//   fwd X W t BT H V C dt loss rl ws wsb err              -> status of check_fwd
+//   orpo X W t ns T H V C dt loss sl dX dW ws wsb err     -> status of check_orpo
+//   ce lg t BT V loss rl ws wsb err                       -> status of check_ce
+//   layout BT H V C dt                                    -> "ok" or the broken layout invariant
+//   query BT H V C dt                                     -> the size queries of flce.h, comma-separated
+// Pointers are plain integers (never dereferenced); 0 is a null pointer.
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/flce.h"
+#include "../../linear_cross_entropy_05_amd/csrc/flce_host.h"
+
+namespace {
+
+const void* P(unsigned long long v) { return reinterpret_cast<const void*>((uintptr_t)v); }
+template <typename T>
+const T* PT(unsigned long long v) {
+  return reinterpret_cast<const T*>((uintptr_t)v);
+}
+
+bool a256(size_t x) { return (x & 255) == 0; }
+
+// Invariants of the forward+backward layout: 256-byte aligned, disjoint
+// regions in order, each large enough for what the kernels put there.
+std::string check_layout(const flce::Layout& L, int64_t BT, int64_t H, int64_t V, int64_t C_req) {
+  const size_t es = (size_t)L.esize;
+  if (L.ldz % flce::kTile || L.ldz < V || L.nvt * flce::kTile != L.ldz) return "ldz/nvt";
+  if (L.C < 1 || (BT > 0 && L.C > BT)) return "chunk range";
+  if (C_req <= 0 && BT > 0 && L.C > flce::kTile && (size_t)L.C * L.ldz * es > ((size_t)1 << 30))
+    return "chunk above 1 GiB";
+  if (L.splits < 1 || L.splits > 16) return "splits";
+  if (L.ldxt < L.C || L.ldxt % 64) return "ldxt";
+  const size_t offs[] = {L.off_nvalid, L.off_lse, L.off_rowloss, L.off_part, L.off_chunk, L.off_dxpart, L.total};
+  for (size_t o : offs)
+    if (!a256(o)) return "unaligned offset";
+  if (L.off_nvalid + 16 > L.off_lse) return "nvalid region";
+  if (L.off_lse + (size_t)L.C * 4 > L.off_rowloss) return "lse region";
+  if (L.off_rowloss + (size_t)(BT > 0 ? BT : 1) * 4 > L.off_part) return "rowloss region";
+  const size_t stats = (size_t)L.C * 2 * L.nvt * 8;
+  const size_t xt = L.dtype == FLCE_BF16 ? (size_t)H * L.ldxt * 2 : 0;
+  if (L.off_part + stats > L.off_chunk || L.off_part + xt > L.off_chunk) return "statistics region";
+  if (L.off_chunk + (size_t)L.C * L.ldz * es > L.off_dxpart) return "chunk region";
+  if (L.splits > 1 && L.off_dxpart + (size_t)L.splits * L.C * H * 4 > L.total) return "dx partials region";
+  if (L.off_dxpart > L.total) return "total";
+  return "ok";
+}
+
+std::string check_fwd_layout(const flce::Layout& L, int64_t BT) {
+  const size_t offs[] = {L.off_nvalid, L.off_lse, L.off_rowloss, L.off_part, L.off_chunk, L.total};
+  for (size_t o : offs)
+    if (!a256(o)) return "fwd unaligned offset";
+  if (L.C < 1 || (BT > 0 && L.C > BT)) return "fwd pass range";
+  if (L.off_lse + (size_t)L.C * 4 > L.off_rowloss) return "fwd lse region";
+  if (L.off_rowloss + (size_t)(BT > 0 ? BT : 1) * 4 > L.off_part) return "fwd rowloss region";
+  if (L.off_part + (size_t)L.C * 2 * L.nvt * 8 > L.total) return "fwd statistics region";
+  if (L.off_chunk != L.total || L.off_dxpart != L.total) return "fwd has a chunk";
+  return "ok";
+}
+
+}  // namespace
+
+int main() {
+  char line[1024];
+  while (fgets(line, sizeof line, stdin)) {
+    char op[32];
+    if (sscanf(line, "%31s", op) != 1) continue;
+    unsigned long long X, W, t, s, loss, rl, dX, dW, ws, wsb, err, lg, sl;
+    long long BT, H, V, C, ns, T;
+    int dt;
+    if (!strcmp(op, "fwd_bwd") &&
+        sscanf(line, "%*s %llu %llu %llu %llu %lld %lld %lld %lld %d %llu %llu %llu %llu %llu %llu %llu", &X, &W, &t,
+               &s, &BT, &H, &V, &C, &dt, &loss, &rl, &dX, &dW, &ws, &wsb, &err) == 16) {
+      flce::Layout L;
+      printf("%d\n", flce::check_fwd_bwd(P(X), P(W), PT<int64_t>(t), PT<float>(s), BT, H, V, C, dt, PT<float>(loss),
+                                         PT<float>(rl), P(dX), PT<float>(dW), P(ws), (size_t)wsb, PT<int32_t>(err),
+                                         &L));
+    } else if (!strcmp(op, "fwd") &&
+               sscanf(line, "%*s %llu %llu %llu %lld %lld %lld %lld %d %llu %llu %llu %llu %llu", &X, &W, &t, &BT, &H,
+                      &V, &C, &dt, &loss, &rl, &ws, &wsb, &err) == 13) {
+      flce::Layout L;
+      printf("%d\n", flce::check_fwd(P(X), P(W), PT<int64_t>(t), BT, H, V, C, dt, PT<float>(loss), PT<float>(rl),
+                                     P(ws), (size_t)wsb, PT<int32_t>(err), &L));
+    } else if (!strcmp(op, "orpo") &&
+               sscanf(line, "%*s %llu %llu %llu %lld %lld %lld %lld %lld %d %llu %llu %llu %llu %llu %llu %llu", &X, &W,
+                      &t, &ns, &T, &H, &V, &C, &dt, &loss, &sl, &dX, &dW, &ws, &wsb, &err) == 16) {
+      flce::OrpoLayout L;
+      printf("%d\n", flce::check_orpo(P(X), P(W), PT<int64_t>(t), ns, T, H, V, C, dt, PT<float>(loss), PT<float>(sl),
+                                      P(dX), PT<float>(dW), P(ws), (size_t)wsb, PT<int32_t>(err), &L));
+    } else if (!strcmp(op, "ce") && sscanf(line, "%*s %llu %llu %lld %lld %llu %llu %llu %llu %llu", &lg, &t, &BT, &V,
+                                           &loss, &rl, &ws, &wsb, &err) == 9) {
+      printf("%d\n", flce::check_ce(PT<float>(lg), PT<int64_t>(t), BT, V, PT<float>(loss), PT<float>(rl), P(ws),
+                                    (size_t)wsb, PT<int32_t>(err)));
+    } else if (!strcmp(op, "layout") && sscanf(line, "%*s %lld %lld %lld %lld %d", &BT, &H, &V, &C, &dt) == 5) {
+      std::string r = check_layout(flce::make_layout(BT, H, V, C, dt), BT, H, V, C);
+      if (r == "ok") r = check_fwd_layout(flce::make_fwd_layout(BT, H, V, C, dt), BT);
+      if (r == "ok" && BT >= 2 && BT % 2 == 0) {
+        const flce::OrpoLayout O = flce::make_orpo_layout(2, BT / 2, H, V, C, dt);
+        const size_t region = O.fwd.total > O.fb.total ? O.fwd.total : O.fb.total;
+        if (O.off_region + region != O.total || !a256(O.off_region) ||
+            O.off_scale + (size_t)BT * 4 > O.off_scratch || O.off_rowloss + (size_t)BT * 4 > O.off_scale)
+          r = "orpo layout";
+      }
+      if (r == "ok" && flce_workspace_bytes(BT, H, V, C, dt) != (BT < 0 ? 0 : flce::make_layout(BT, H, V, C, dt).total))
+        r = "workspace query";
+      printf("%s\n", r.c_str());
+    } else if (!strcmp(op, "query") && sscanf(line, "%*s %lld %lld %lld %lld %d", &BT, &H, &V, &C, &dt) == 5) {
+      printf("%lld,%zu,%zu,%zu,%zu\n", (long long)flce_chunk_tokens(BT, H, V, C, dt),
+             flce_workspace_bytes(BT, H, V, C, dt), flce_fwd_workspace_bytes(BT, H, V, C, dt),
+             flce_orpo_workspace_bytes(2, BT, H, V, C, dt), ce_workspace_bytes(BT, V));
+    } else {
+      printf("bad line\n");
+    }
+    fflush(stdout);
+  }
+  return 0;
+}

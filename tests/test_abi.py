@@ -68,9 +68,15 @@ def test_workspace_bound_by_one_chunk(lib):
     assert lib.ce_workspace_bytes(8192, 256000) >= 8192 * 4
 
 
+# Default (fake, never dereferenced) arguments of each entry point and the
+# cases that must be rejected on the host with the given status.  The same
+# tables drive the sanitizer build of the host checks (test_host_sanitize.py).
+FWD_BWD_DEFAULTS = dict(X=16, W=16, t=16, s=None, BT=8, H=128, V=256, ign=-100, C=0, dt=F32, loss=16, rl=None, dX=16,
+                        dW=16, ws=256, wsb=1 << 20, err=16, stream=None)
+
+
 def _call(lib, **kw):
-    a = dict(X=16, W=16, t=16, s=None, BT=8, H=128, V=256, ign=-100, C=0, dt=F32, loss=16, rl=None, dX=16, dW=16,
-             ws=256, wsb=1 << 20, err=16, stream=None)
+    a = dict(FWD_BWD_DEFAULTS)
     a.update(kw)
     vp = ctypes.c_void_p
     return lib.flce_fwd_bwd(vp(a["X"]), vp(a["W"]), vp(a["t"]), vp(a["s"]), a["BT"], a["H"], a["V"], a["ign"], a["C"],
@@ -78,80 +84,83 @@ def _call(lib, **kw):
                             vp(a["err"]), vp(a["stream"]))
 
 
-@pytest.mark.parametrize(
-    "kw,status",
-    [
-        (dict(dt=5), 2),
-        (dict(H=0), 1),
-        (dict(V=0), 1),
-        (dict(BT=-1), 1),
-        (dict(W=None), 1),
-        (dict(X=None), 1),
-        (dict(t=None), 1),
-        (dict(loss=None), 1),
-        (dict(dX=None), 1),
-        (dict(dW=None), 1),
-        (dict(ws=None), 1),
-        (dict(err=None), 1),
-        (dict(H=130), 7),
-        (dict(H=132, dt=BF16), 7),
-        (dict(X=24), 8),
-        (dict(W=8), 8),
-        (dict(ws=128), 8),
-        (dict(t=20), 8),
-        (dict(s=18), 8),
-        # the products store 16-byte (fp32) or 8-byte (bf16) pieces of dX and dW rows
-        (dict(dX=20), 8),
-        (dict(dX=24, dt=BF16, H=128), 8),
-        (dict(dW=20), 8),
-        (dict(wsb=16), 3),
-        # a 256-row tile of the logits chunk past 2^31 bytes (V = 4.2 M bf16, 2.1 M fp32)
-        (dict(V=4_200_000, dt=BF16, C=1, wsb=1 << 62), 7),
-        (dict(V=2_100_000, C=1, wsb=1 << 62), 7),
-        # a 256-row tile of W past 2^31 bytes (H = 4.2 M bf16)
-        (dict(H=4_200_000, dt=BF16, C=1, wsb=1 << 62), 7),
-        # the transposed token chunk (bf16 only): chunk of 4.2 M tokens
-        (dict(BT=4_200_000, H=8, dt=BF16, C=4_200_000, wsb=1 << 62), 7),
-    ],
-)
+FWD_BWD_CASES = [
+    (dict(dt=5), 2),
+    (dict(H=0), 1),
+    (dict(V=0), 1),
+    (dict(BT=-1), 1),
+    (dict(W=None), 1),
+    (dict(X=None), 1),
+    (dict(t=None), 1),
+    (dict(loss=None), 1),
+    (dict(dX=None), 1),
+    (dict(dW=None), 1),
+    (dict(ws=None), 1),
+    (dict(err=None), 1),
+    (dict(H=130), 7),
+    (dict(H=132, dt=BF16), 7),
+    (dict(X=24), 8),
+    (dict(W=8), 8),
+    (dict(ws=128), 8),
+    (dict(t=20), 8),
+    (dict(s=18), 8),
+    # the products store 16-byte (fp32) or 8-byte (bf16) pieces of dX and dW rows
+    (dict(dX=20), 8),
+    (dict(dX=24, dt=BF16, H=128), 8),
+    (dict(dW=20), 8),
+    (dict(wsb=16), 3),
+    # a 256-row tile of the logits chunk past 2^31 bytes (V = 4.2 M bf16, 2.1 M fp32)
+    (dict(V=4_200_000, dt=BF16, C=1, wsb=1 << 62), 7),
+    (dict(V=2_100_000, C=1, wsb=1 << 62), 7),
+    # a 256-row tile of W past 2^31 bytes (H = 4.2 M bf16)
+    (dict(H=4_200_000, dt=BF16, C=1, wsb=1 << 62), 7),
+    # the transposed token chunk (bf16 only): chunk of 4.2 M tokens
+    (dict(BT=4_200_000, H=8, dt=BF16, C=4_200_000, wsb=1 << 62), 7),
+]
+
+
+@pytest.mark.parametrize("kw,status", FWD_BWD_CASES)
 def test_host_argument_checks(lib, kw, status):
     # fake, never-dereferenced addresses: every case is rejected on the host
     assert _call(lib, **kw) == status
 
 
+FWD_DEFAULTS = dict(X=16, W=16, t=16, BT=8, H=128, V=256, ign=-100, C=0, dt=F32, loss=16, rl=None, ws=256,
+                    wsb=1 << 20, err=16, stream=None)
+
+
 def _call_fwd(lib, **kw):
-    a = dict(X=16, W=16, t=16, BT=8, H=128, V=256, ign=-100, C=0, dt=F32, loss=16, rl=None, ws=256, wsb=1 << 20,
-             err=16, stream=None)
+    a = dict(FWD_DEFAULTS)
     a.update(kw)
     vp = ctypes.c_void_p
     return lib.flce_fwd(vp(a["X"]), vp(a["W"]), vp(a["t"]), a["BT"], a["H"], a["V"], a["ign"], a["C"], a["dt"],
                         vp(a["loss"]), vp(a["rl"]), vp(a["ws"]), a["wsb"], vp(a["err"]), vp(a["stream"]))
 
 
-@pytest.mark.parametrize(
-    "kw,status",
-    [
-        (dict(dt=5), 2),
-        (dict(H=0), 1),
-        (dict(V=0), 1),
-        (dict(BT=-1), 1),
-        (dict(W=None), 1),
-        (dict(X=None), 1),
-        (dict(t=None), 1),
-        (dict(loss=None), 1),
-        (dict(ws=None), 1),
-        (dict(err=None), 1),
-        (dict(H=130), 7),
-        (dict(H=132, dt=BF16), 7),
-        (dict(X=24), 8),
-        (dict(W=8), 8),
-        (dict(ws=128), 8),
-        (dict(t=20), 8),
-        (dict(rl=18), 8),
-        (dict(H=4_200_000, dt=BF16, C=1, wsb=1 << 62), 7),
-        (dict(wsb=16), 3),
-    ],
-)
+FWD_CASES = [
+    (dict(dt=5), 2),
+    (dict(H=0), 1),
+    (dict(V=0), 1),
+    (dict(BT=-1), 1),
+    (dict(W=None), 1),
+    (dict(X=None), 1),
+    (dict(t=None), 1),
+    (dict(loss=None), 1),
+    (dict(ws=None), 1),
+    (dict(err=None), 1),
+    (dict(H=130), 7),
+    (dict(H=132, dt=BF16), 7),
+    (dict(X=24), 8),
+    (dict(W=8), 8),
+    (dict(ws=128), 8),
+    (dict(t=20), 8),
+    (dict(rl=18), 8),
+    (dict(H=4_200_000, dt=BF16, C=1, wsb=1 << 62), 7),
+    (dict(wsb=16), 3),
+]
+
+
+@pytest.mark.parametrize("kw,status", FWD_CASES)
 def test_forward_host_argument_checks(lib, kw, status):
     assert _call_fwd(lib, **kw) == status
 
@@ -167,16 +176,25 @@ def test_forward_workspace_has_no_chunk_buffer(lib):
     assert lib.flce_fwd_workspace_bytes(8, 128, 256, 0, 9) == 0
 
 
-def test_ce_host_argument_checks(lib):
+CE_DEFAULTS = dict(lg=16, t=16, BT=4, V=10, ign=-100, loss=16, rl=None, ws=256, wsb=4096, err=16, stream=None)
+CE_CASES = [
+    (dict(BT=-1), 1),
+    (dict(V=0), 1),
+    (dict(V=1 << 31), 1),  # V >= 2^31
+    (dict(lg=None), 1),
+    (dict(loss=None), 1),
+    (dict(lg=18), 8),
+    (dict(wsb=1), 3),
+]
+
+
+@pytest.mark.parametrize("kw,status", CE_CASES)
+def test_ce_host_argument_checks(lib, kw, status):
+    a = dict(CE_DEFAULTS)
+    a.update(kw)
     vp = ctypes.c_void_p
-    f = lib.ce_fwd_bwd_inplace
-    assert f(vp(16), vp(16), -1, 10, -100, vp(16), vp(0), vp(256), 4096, vp(16), vp(0)) == 1
-    assert f(vp(16), vp(16), 4, 0, -100, vp(16), vp(0), vp(256), 4096, vp(16), vp(0)) == 1
-    assert f(vp(16), vp(16), 4, 1 << 31, -100, vp(16), vp(0), vp(256), 4096, vp(16), vp(0)) == 1  # V >= 2^31
-    assert f(vp(0), vp(16), 4, 10, -100, vp(16), vp(0), vp(256), 4096, vp(16), vp(0)) == 1
-    assert f(vp(16), vp(16), 4, 10, -100, vp(0), vp(0), vp(256), 4096, vp(16), vp(0)) == 1
-    assert f(vp(18), vp(16), 4, 10, -100, vp(16), vp(0), vp(256), 4096, vp(16), vp(0)) == 8
-    assert f(vp(16), vp(16), 4, 10, -100, vp(16), vp(0), vp(256), 1, vp(16), vp(0)) == 3
+    assert lib.ce_fwd_bwd_inplace(vp(a["lg"]), vp(a["t"]), a["BT"], a["V"], a["ign"], vp(a["loss"]), vp(a["rl"]),
+                                  vp(a["ws"]), a["wsb"], vp(a["err"]), vp(a["stream"])) == status
 
 
 def test_no_cpu_fallback_in_product_code():
@@ -190,9 +208,12 @@ def test_no_cpu_fallback_in_product_code():
         assert "synth_inputs" not in text, p
 
 
+ORPO_DEFAULTS = dict(X=16, W=16, t=16, ns=4, T=8, H=128, V=256, ign=-100, beta=0.1, C=0, dt=F32, loss=16, sl=None,
+                     dX=16, dW=16, ws=256, wsb=1 << 24, err=16, stream=None)
+
+
 def _call_orpo(lib, **kw):
-    a = dict(X=16, W=16, t=16, ns=4, T=8, H=128, V=256, ign=-100, beta=0.1, C=0, dt=F32, loss=16, sl=None, dX=16,
-             dW=16, ws=256, wsb=1 << 24, err=16, stream=None)
+    a = dict(ORPO_DEFAULTS)
     a.update(kw)
     vp = ctypes.c_void_p
     return lib.flce_orpo(vp(a["X"]), vp(a["W"]), vp(a["t"]), a["ns"], a["T"], a["H"], a["V"], a["ign"],
@@ -200,25 +221,25 @@ def _call_orpo(lib, **kw):
                          vp(a["dW"]), vp(a["ws"]), a["wsb"], vp(a["err"]), vp(a["stream"]))
 
 
-@pytest.mark.parametrize(
-    "kw,status",
-    [
-        (dict(dt=3), 2),
-        (dict(ns=3), 1),
-        (dict(ns=0), 1),
-        (dict(T=0), 1),
-        (dict(H=0), 1),
-        (dict(X=None), 1),
-        (dict(dX=None), 1),
-        (dict(H=130), 7),
-        (dict(X=24), 8),
-        (dict(sl=18), 8),
-        (dict(dX=24), 8),
-        (dict(dW=20), 8),
-        (dict(ws=128), 8),
-        (dict(wsb=16), 3),
-    ],
-)
+ORPO_CASES = [
+    (dict(dt=3), 2),
+    (dict(ns=3), 1),
+    (dict(ns=0), 1),
+    (dict(T=0), 1),
+    (dict(H=0), 1),
+    (dict(X=None), 1),
+    (dict(dX=None), 1),
+    (dict(H=130), 7),
+    (dict(X=24), 8),
+    (dict(sl=18), 8),
+    (dict(dX=24), 8),
+    (dict(dW=20), 8),
+    (dict(ws=128), 8),
+    (dict(wsb=16), 3),
+]
+
+
+@pytest.mark.parametrize("kw,status", ORPO_CASES)
 def test_orpo_host_argument_checks(lib, kw, status):
     assert _call_orpo(lib, **kw) == status
 

@@ -91,3 +91,36 @@ def test_orpo_module_autograd():
     assert Xg.grad.shape == (n_seq, T, H) and Wg.grad.dtype == torch.bfloat16
     assert rel_err(to_np(Xg.grad).reshape(-1, H), 2.0 * ref["dX"]) <= tg
     assert rel_err(to_np(Wg.grad), 2.0 * ref["dW"]) <= tg
+
+
+def test_orpo_near_certain_chosen_sequence():
+    """A chosen sequence with one valid token whose target logit exceeds all
+    others by 25: its loss in fp32 rounds to 0 (or just below), so its mean
+    log-probability is 0 where the float64 oracle has ~-2e-10.  The odds term
+    must stay finite and the results match the oracle (its limits as a -> 0
+    are finite)."""
+    import linear_cross_entropy_05_amd as flce
+
+    n_seq, T, H, V = 4, 8, 8, 16
+    w, X, W, y = _inputs(n_seq, T, H, V, "fp32", seed=76)
+    t = int(y[0]) if int(y[0]) != w.ignore_index else 3
+    y[0] = t
+    y[1:T] = w.ignore_index               # sequence 0: one valid token
+    X[0] = 0.0
+    X[0, 0] = 25.0                        # x_0 = 25 e_0
+    W[:, 0] = 0.0
+    W[t, 0] = 1.0                         # z_{0,t} = 25, every other logit of token 0 is 0
+    dev = torch.device("cuda", 0)
+    say(f"[gpu] flce_orpo near-certain chosen sequence n_seq={n_seq} T={T} H={H} V={V} fp32")
+    loss, dX, dW, sl = flce.flce_orpo(X.to(dev), W.to(dev), y.to(dev).view(n_seq, T), 0.1, w.ignore_index,
+                                      seq_logp=True)
+    torch.cuda.synchronize()
+    ref = oracle.orpo_ref(X, W, y, n_seq, 0.1, w.ignore_index)
+    assert -1e-9 < ref["seq_logp"][0] < 0.0  # float64 resolves the near-certain score
+    assert bool(torch.isfinite(loss)) and bool(torch.isfinite(dX).all()) and bool(torch.isfinite(dW).all())
+    tl, tg = TOL["fp32"]
+    el = abs(loss.item() - ref["loss"]) / abs(ref["loss"])
+    ex, ew = rel_err(to_np(dX), ref["dX"]), rel_err(to_np(dW), ref["dW"])
+    say(f"  loss {loss.item():.7f} ref {ref['loss']:.7f} err {el:.2e}; dX {ex:.2e}; dW {ew:.2e}; "
+        f"a_0 gpu {float(sl[0]):.3e} ref {ref['seq_logp'][0]:.3e}")
+    assert el <= tl and ex <= tg and ew <= tg

@@ -163,3 +163,24 @@ def test_token_scale_one_over_n_is_the_mean():
     b = oracle.flce_ref(X, W, y, -100, token_scale=np.full(len(y), 1.0 / n))
     assert float(np.max(np.abs(a["dX"] - b["dX"]))) <= 1e-15 * float(np.max(np.abs(a["dX"])))
     assert float(np.max(np.abs(a["dW"] - b["dW"]))) <= 1e-15 * float(np.max(np.abs(a["dW"])))
+
+
+def test_rowblock_oracle_equals_whole_oracle():
+    """The row-blocked form (for hosts short of memory) against the whole
+    definition, with blocks that do not divide the batch and ignored rows in
+    several blocks; also the all-ignored batch."""
+    import synth_inputs as si
+
+    w = si.small(37, 24, 50, "fp32", seed=11, ignore=("random_frac", 0.2))
+    X, W, y = si.make_inputs(w)
+    full = oracle.flce_ref(X, W, y, w.ignore_index)
+    for block in (1, 5, 16, 37, 100):
+        part = oracle.flce_ref_rowblocks(X, W, y, w.ignore_index, block=block)
+        assert abs(part["loss"] - full["loss"]) <= 1e-14 * abs(full["loss"])
+        for k in ("dX", "dW", "row_loss", "lse"):
+            assert np.max(np.abs(part[k] - full[k])) <= 1e-13 * np.max(np.abs(full[k])), (block, k)
+        assert part["n_valid"] == full["n_valid"]
+    y2 = y.clone()
+    y2[:] = w.ignore_index
+    part = oracle.flce_ref_rowblocks(X, W, y2, w.ignore_index, block=8)
+    assert part["loss"] == 0.0 and not part["dX"].any() and not part["dW"].any()

@@ -43,6 +43,30 @@ def test_two_class_repeated_tokens():
     assert np.allclose(out["seq_logp"], [-sp(-v) for v in c], rtol=1e-14, atol=0)
 
 
+def test_two_class_near_certain_chosen():
+    """The two-class closed form where one chosen sequence is near certain
+    (logit 20: a = log sigmoid(20) ~ -2e-9), the regime where log(1 - e^a)
+    is steep.  Loss and the per-token factors dL/dl_i against closed forms:
+    with one token per sequence e^{a_s} = sigmoid(c_s), r_p = c_w - c_l and
+    dL/dl_w = 1/B + beta/B sigmoid(-r_p) / sigmoid(-c_w),
+    dL/dl_l = -beta/B sigmoid(-r_p) / sigmoid(-c_l)."""
+    c = np.array([20.0, -0.4, 2.0, 0.7])  # B = 2: chosen 0, 1; rejected 2, 3
+    X = np.stack([c, np.zeros_like(c)], axis=1)
+    W = np.array([[0.0, 0.0], [1.0, 0.0]])
+    y = np.ones(4, dtype=np.int64)
+    beta = 0.5
+    out = orpo_ref(X, W, y, n_seq=4, beta=beta)
+    sp = lambda x: math.log1p(math.exp(-abs(x))) + max(x, 0.0)  # noqa: E731
+    sig = lambda x: 1.0 / (1.0 + math.exp(-x))  # noqa: E731
+    r = [c[0] - c[2], c[1] - c[3]]
+    expect = (sp(-c[0]) + sp(-c[1])) / 2 + beta * (sp(-r[0]) + sp(-r[1])) / 2
+    assert abs(out["loss"] - expect) <= 1e-12 * expect, (out["loss"], expect)
+    w = [1 / 2 + beta / 2 * sig(-r[p]) / sig(-c[p]) for p in range(2)]
+    w += [-beta / 2 * sig(-r[p]) / sig(-c[2 + p]) for p in range(2)]
+    # a_w is resolved to ~1e-6 relative in float64 (lse - z at |z| = 20)
+    assert np.allclose(out["weights"], w, rtol=1e-5, atol=0), (out["weights"], w)
+
+
 def _case(seed, n_seq=4, T=3, H=4, V=6, n_ignore=2):
     r = np.random.default_rng(seed)
     X = r.standard_normal((n_seq * T, H))
