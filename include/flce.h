@@ -66,7 +66,8 @@ enum flce_status {
   FLCE_ERR_LAUNCH = 5,    /* a kernel launch failed */
   FLCE_ERR_TARGET = 6,    /* (device-side, via *err_flag) target out of range */
   FLCE_ERR_SHAPE = 7,     /* H not a multiple of 8 (bf16) or 4 (fp32), or a 256-row tile too large (below) */
-  FLCE_ERR_ALIGN = 8      /* X, W, dX or dW not 16-byte aligned, workspace not 256, targets not 8 */
+  FLCE_ERR_ALIGN = 8,     /* X, W, dX or dW not 16-byte aligned, workspace not 256, targets not 8 */
+  FLCE_ERR_SCRATCH = 9    /* more rows than ce_fwd_bwd_inplace_noalloc's static scratch holds */
 };
 
 /* Tokens per chunk that flce_fwd_bwd will use: chunk_tokens if positive
@@ -174,6 +175,24 @@ size_t ce_workspace_bytes(int64_t BT, int64_t V);
 int ce_fwd_bwd_inplace(float* logits, const int64_t* targets, int64_t BT, int64_t V, int64_t ignore_index,
                        float* loss, float* row_loss, void* workspace, size_t workspace_bytes, int32_t* err_flag,
                        void* stream);
+
+/* ce_fwd_bwd_inplace without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  It allocates nothing: its scratch (the valid-token
+ * count and, when row_loss is NULL, one float per row) is a static device
+ * array of 256 + 4 * ce_noalloc_max_rows() bytes (8 MiB + 256 B) that each
+ * GPU holds for the life of the process.  The first call on a device looks
+ * up that array's address there (no allocation, no stream work).
+ *   BT <= ce_noalloc_max_rows() (2^21); more rows return FLCE_ERR_SCRATCH
+ *   before anything is launched.  Other arguments, results and errors as for
+ *   ce_fwd_bwd_inplace.
+ * All calls on one GPU share its scratch: calls that overlap on that GPU
+ * (several streams or host threads at once) race and give undefined results;
+ * serialise them.  Nothing needs clearing between calls: every scratch word
+ * a call reads is written earlier in the same call. */
+int64_t ce_noalloc_max_rows(void);
+int ce_fwd_bwd_inplace_noalloc(float* logits, const int64_t* targets, int64_t BT, int64_t V, int64_t ignore_index,
+                               float* loss, float* row_loss, int32_t* err_flag, void* stream);
 
 /* Per-kernel timing, for benchmarks and profilers (process-global, not
  * thread-safe, off by default).  flce_profile_begin(max_launches) creates

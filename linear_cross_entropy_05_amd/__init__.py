@@ -5,6 +5,7 @@ Public API (all GPU-only; the HIP library must be built):
     flce_forward(X, W, targets, ignore_index=-100) -> loss   (forward only)
     flce_orpo(X, W, targets, beta=0.1) -> loss, dX, dW                (fused-linear ORPO)
     ce_fwd_bwd_inplace(logits, targets, ignore_index=-100) -> loss
+    ce_fwd_bwd_inplace_noalloc(logits, targets, ...) -> loss   (no allocation; static scratch)
     FusedLinearCrossEntropyLoss(ignore_index=-100, reduction="mean"|"none")(weight, input, target) -> loss
 """
 from .binding import (  # noqa: F401
@@ -13,6 +14,8 @@ from .binding import (  # noqa: F401
     FusedLinearORPOLoss,
     KernelTimer,
     ce_fwd_bwd_inplace,
+    ce_fwd_bwd_inplace_noalloc,
+    ce_noalloc_max_rows,
     ce_workspace_bytes,
     flce_chunk_tokens,
     flce_forward,

@@ -34,6 +34,7 @@ STATUS = {
     6: "FLCE_ERR_TARGET",
     7: "FLCE_ERR_SHAPE",
     8: "FLCE_ERR_ALIGN",
+    9: "FLCE_ERR_SCRATCH",
 }
 _DTYPES = {torch.float32: FLCE_F32, torch.bfloat16: FLCE_BF16}
 
@@ -69,6 +70,10 @@ def _declare(lib):
     lib.ce_workspace_bytes.restype = sz
     lib.ce_fwd_bwd_inplace.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, sz, vp, vp]
     lib.ce_fwd_bwd_inplace.restype = c.c_int
+    lib.ce_noalloc_max_rows.argtypes = []
+    lib.ce_noalloc_max_rows.restype = i64
+    lib.ce_fwd_bwd_inplace_noalloc.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp, vp]
+    lib.ce_fwd_bwd_inplace_noalloc.restype = c.c_int
     lib.flce_status_str.argtypes = [c.c_int]
     lib.flce_status_str.restype = c.c_char_p
     lib.flce_device_supported.argtypes = [c.c_int]
@@ -326,6 +331,45 @@ def ce_fwd_bwd_inplace(logits, targets, ignore_index: int = -100, *, row_loss: b
     if check:
         check_err_flag(err, "ce_fwd_bwd_inplace")
     return (loss, rl) if row_loss else loss
+
+
+def ce_fwd_bwd_inplace_noalloc(logits, targets, ignore_index: int = -100, *, out=None, row_loss=None,
+                               check: bool = True):
+    """ce_fwd_bwd_inplace through the entry point that allocates nothing
+    (its scratch is a static device array; at most ce_noalloc_max_rows()
+    rows).  ``out`` may pass preallocated (loss fp32 0-d, err int32 [1])
+    tensors and ``row_loss`` an fp32 [BT] tensor to fill; with both given,
+    this wrapper allocates nothing either.  Calls that overlap on one GPU
+    share its scratch and must be serialised.  Returns the loss tensor."""
+    lib = load_library()
+    _check_tensor("logits", logits, dtype=torch.float32, ndim=2)
+    _check_tensor("targets", targets, dtype=torch.int64, ndim=1)
+    BT, V = logits.shape
+    if targets.shape[0] != BT:
+        raise ValueError("targets length must equal logits rows")
+    dev = logits.device
+    _same_device(dev, targets=targets)
+    if out is None:
+        loss = torch.empty((), dtype=torch.float32, device=dev)
+        err = torch.empty((1,), dtype=torch.int32, device=dev)
+    else:
+        loss, err = out
+        _check_out("out loss", loss, (), torch.float32, dev)
+        _check_out("out err", err, (1,), torch.int32, dev)
+    if row_loss is not None:
+        _check_out("row_loss", row_loss, (BT,), torch.float32, dev)
+    with torch.cuda.device(dev):
+        st = lib.ce_fwd_bwd_inplace_noalloc(_ptr(logits), _ptr(targets), BT, V, ignore_index, _ptr(loss),
+                                            _ptr(row_loss), _ptr(err), _stream(dev))
+    if st != 0:
+        raise FlceError(st, "ce_fwd_bwd_inplace_noalloc")
+    if check:
+        check_err_flag(err, "ce_fwd_bwd_inplace_noalloc")
+    return loss
+
+
+def ce_noalloc_max_rows() -> int:
+    return int(load_library().ce_noalloc_max_rows())
 
 
 KERNEL_KINDS = ["count_valid", "logits", "lse", "grad_inplace", "dx", "dx_reduce", "dw", "loss_final",

@@ -15,6 +15,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/flce.h"
 #include "flce_internal.h"
@@ -157,6 +158,65 @@ int ce_fwd_bwd_inplace(float* logits, const int64_t* targets, int64_t BT, int64_
   char* ws = static_cast<char*>(workspace);
   int32_t* nvalid = reinterpret_cast<int32_t*>(ws);
   float* rl = row_loss ? row_loss : reinterpret_cast<float*>(ws + 256);
+  if (flce::launch_count_valid(targets, BT, V, ignore_index, nvalid, err_flag, s) != hipSuccess)
+    return FLCE_ERR_LAUNCH;
+  if (flce::launch_ce_rows(logits, targets, BT, V, ignore_index, nvalid, rl, s) != hipSuccess)
+    return FLCE_ERR_LAUNCH;
+  if (flce::launch_loss_final(rl, BT, nvalid, loss, s) != hipSuccess) return FLCE_ERR_LAUNCH;
+  return FLCE_OK;
+}
+
+// ---- logits-only cross-entropy with no workspace and no allocation ----------
+
+namespace {
+
+// The one scratch array of ce_fwd_bwd_inplace_noalloc: the valid-token count
+// (first 256 bytes) and, when the caller passes no row_loss, one float of
+// token loss per row.  Each GPU the library runs on holds its own copy for
+// the life of the process.
+constexpr int64_t kNoAllocMaxRows = (int64_t)1 << 21;
+constexpr size_t kNoAllocScratchBytes = 256 + (size_t)kNoAllocMaxRows * 4;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+// Device address of `scratch` on each device, looked up once per device with
+// that device current (the array's name is only a host-side stand-in).
+std::atomic<char*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+char* scratch_on(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  char* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    p = static_cast<char*>(q);
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
+int64_t ce_noalloc_max_rows(void) { return kNoAllocMaxRows; }
+
+int ce_fwd_bwd_inplace_noalloc(float* logits, const int64_t* targets, int64_t BT, int64_t V, int64_t ignore_index,
+                               float* loss, float* row_loss, int32_t* err_flag, void* stream) {
+  const int st = flce::check_ce_noalloc(logits, targets, BT, V, loss, row_loss, err_flag, kNoAllocMaxRows);
+  if (st != FLCE_OK) return st;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev >= kMaxDevices) return FLCE_ERR_DEVICE;
+  if (device_status(dev) != 1) return FLCE_ERR_DEVICE;
+  char* ws = scratch_on(dev);
+  if (!ws) return FLCE_ERR_LAUNCH;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* nvalid = reinterpret_cast<int32_t*>(ws);
+  float* rl = row_loss ? row_loss : reinterpret_cast<float*>(ws + 256);
+  // every scratch word read is written first in stream order (count, then
+  // token losses), so nothing needs clearing between calls
   if (flce::launch_count_valid(targets, BT, V, ignore_index, nvalid, err_flag, s) != hipSuccess)
     return FLCE_ERR_LAUNCH;
   if (flce::launch_ce_rows(logits, targets, BT, V, ignore_index, nvalid, rl, s) != hipSuccess)

@@ -67,5 +67,8 @@ int check_orpo(const void* X, const void* W, const int64_t* targets, int64_t n_s
                OrpoLayout* L);
 int check_ce(const float* logits, const int64_t* targets, int64_t BT, int64_t V, const float* loss,
              const float* row_loss, const void* workspace, size_t workspace_bytes, const int32_t* err_flag);
+// the logits-only cross-entropy with no workspace: at most max_rows rows
+int check_ce_noalloc(const float* logits, const int64_t* targets, int64_t BT, int64_t V, const float* loss,
+                     const float* row_loss, const int32_t* err_flag, int64_t max_rows);
 
 }  // namespace flce

@@ -233,6 +233,17 @@ int check_ce(const float* logits, const int64_t* targets, int64_t BT, int64_t V,
   return FLCE_OK;
 }
 
+int check_ce_noalloc(const float* logits, const int64_t* targets, int64_t BT, int64_t V, const float* loss,
+                     const float* row_loss, const int32_t* err_flag, int64_t max_rows) {
+  if (!sizes_ok(BT, 1, V)) return FLCE_ERR_ARG;
+  if (BT > max_rows) return FLCE_ERR_SCRATCH;
+  if (!loss || !err_flag) return FLCE_ERR_ARG;
+  if (BT > 0 && (!logits || !targets)) return FLCE_ERR_ARG;
+  if ((logits && !aligned(logits, 4)) || (targets && !aligned(targets, 8)) || (row_loss && !aligned(row_loss, 4)))
+    return FLCE_ERR_ALIGN;
+  return FLCE_OK;
+}
+
 }  // namespace flce
 
 extern "C" {
@@ -250,6 +261,7 @@ const char* flce_status_str(int status) {
       return "unsupported shape (H must be a multiple of 8 for bf16, 4 for fp32; 256 rows of W, of the logits "
              "chunk and of the transposed token chunk must each fit in 2^31 bytes)";
     case FLCE_ERR_ALIGN: return "misaligned pointer";
+    case FLCE_ERR_SCRATCH: return "more rows than the static scratch of the no-allocation entry point holds";
     default: return "unknown status";
   }
 }

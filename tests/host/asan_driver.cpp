@@ -6,6 +6,7 @@
 //   fwd X W t BT H V C dt loss rl ws wsb err              -> status of check_fwd
 //   orpo X W t ns T H V C dt loss sl dX dW ws wsb err     -> status of check_orpo
 //   ce lg t BT V loss rl ws wsb err                       -> status of check_ce
+//   ce_noalloc lg t BT V loss rl err max_rows             -> status of check_ce_noalloc
 //   layout BT H V C dt                                    -> "ok" or the broken layout invariant
 //   query BT H V C dt                                     -> the size queries of flce.h, comma-separated
 // Pointers are plain integers (never dereferenced); 0 is a null pointer.
@@ -98,6 +99,10 @@ int main() {
                                            &loss, &rl, &ws, &wsb, &err) == 9) {
       printf("%d\n", flce::check_ce(PT<float>(lg), PT<int64_t>(t), BT, V, PT<float>(loss), PT<float>(rl), P(ws),
                                     (size_t)wsb, PT<int32_t>(err)));
+    } else if (!strcmp(op, "ce_noalloc") && sscanf(line, "%*s %llu %llu %lld %lld %llu %llu %llu %lld", &lg, &t, &BT,
+                                                  &V, &loss, &rl, &err, &C) == 8) {
+      printf("%d\n", flce::check_ce_noalloc(PT<float>(lg), PT<int64_t>(t), BT, V, PT<float>(loss), PT<float>(rl),
+                                            PT<int32_t>(err), C));
     } else if (!strcmp(op, "layout") && sscanf(line, "%*s %lld %lld %lld %lld %d", &BT, &H, &V, &C, &dt) == 5) {
       std::string r = check_layout(flce::make_layout(BT, H, V, C, dt), BT, H, V, C);
       if (r == "ok") r = check_fwd_layout(flce::make_fwd_layout(BT, H, V, C, dt), BT);

@@ -31,13 +31,15 @@ def test_exports_every_declared_function(lib):
         "flce_chunk_tokens",
         "flce_status_str",
         "flce_device_supported",
+        "ce_fwd_bwd_inplace_noalloc",
+        "ce_noalloc_max_rows",
     }
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings(lib):
-    for s in range(9):
+    for s in range(10):
         assert lib.flce_status_str(s)
     assert b"unknown" in lib.flce_status_str(99)
 
@@ -195,6 +197,34 @@ def test_ce_host_argument_checks(lib, kw, status):
     vp = ctypes.c_void_p
     assert lib.ce_fwd_bwd_inplace(vp(a["lg"]), vp(a["t"]), a["BT"], a["V"], a["ign"], vp(a["loss"]), vp(a["rl"]),
                                   vp(a["ws"]), a["wsb"], vp(a["err"]), vp(a["stream"])) == status
+
+
+NOALLOC_MAX_ROWS = 1 << 21
+NOALLOC_DEFAULTS = dict(lg=16, t=16, BT=4, V=10, ign=-100, loss=16, rl=None, err=16, stream=None)
+NOALLOC_CASES = [
+    (dict(BT=NOALLOC_MAX_ROWS + 1), 9),  # more rows than the static scratch holds
+    (dict(BT=-1), 1),
+    (dict(V=0), 1),
+    (dict(lg=None), 1),
+    (dict(loss=None), 1),
+    (dict(err=None), 1),
+    (dict(lg=18), 8),
+    (dict(rl=18), 8),
+    (dict(t=20), 8),
+]
+
+
+def test_noalloc_row_limit(lib):
+    assert lib.ce_noalloc_max_rows() == NOALLOC_MAX_ROWS
+
+
+@pytest.mark.parametrize("kw,status", NOALLOC_CASES)
+def test_ce_noalloc_host_argument_checks(lib, kw, status):
+    a = dict(NOALLOC_DEFAULTS)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    assert lib.ce_fwd_bwd_inplace_noalloc(vp(a["lg"]), vp(a["t"]), a["BT"], a["V"], a["ign"], vp(a["loss"]),
+                                          vp(a["rl"]), vp(a["err"]), vp(a["stream"])) == status
 
 
 def test_no_cpu_fallback_in_product_code():

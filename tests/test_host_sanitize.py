@@ -65,6 +65,11 @@ def test_entry_point_checks_under_sanitizers(driver):
         a = dict(abi.CE_DEFAULTS, **kw)
         lines.append("ce " + " ".join(str(_p(a[k])) for k in ("lg", "t", "BT", "V", "loss", "rl", "ws", "wsb", "err")))
         want.append(status)
+    for kw, status in abi.NOALLOC_CASES + [({}, 0)]:
+        a = dict(abi.NOALLOC_DEFAULTS, **kw)
+        lines.append("ce_noalloc " + " ".join(str(_p(a[k])) for k in ("lg", "t", "BT", "V", "loss", "rl", "err"))
+                     + f" {abi.NOALLOC_MAX_ROWS}")
+        want.append(status)
     got = [int(x) for x in _run(driver, lines)]
     assert got == want
 
