@@ -107,10 +107,11 @@ size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, int64_t chunk_toke
  * With token_scale NULL the gradients are for an upstream gradient of 1 on the
  * mean loss; scale them for another.
  * Size limits (status FLCE_ERR_SHAPE): the kernels address a 256-row tile with
- * 32-bit byte offsets, so 256 * H * esize, 256 * round_up(V, 256) * esize and,
- * for bf16, 256 * round_up(chunk, 64) * 2 must each be below 2^31 (esize 2 for
- * bf16, 4 for fp32: V up to ~4.19 M for bf16, ~2.09 M for fp32).  flce_fwd
- * checks only the first; flce_orpo checks all three. */
+ * 32-bit byte offsets, so 256 * H * esize, 256 * H * 4 (the fp32 dW),
+ * 256 * round_up(V, 256) * esize and, for bf16, 256 * round_up(chunk, 64) * 2
+ * must each be below 2^31 (esize 2 for bf16, 4 for fp32: V up to ~4.19 M for
+ * bf16, ~2.09 M for fp32; H up to ~2.09 M).  flce_fwd checks only the first;
+ * flce_orpo checks all four. */
 int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, const float* token_scale, int64_t BT,
                  int64_t H, int64_t V, int64_t ignore_index, int64_t chunk_tokens, int dtype, float* loss,
                  float* row_loss, void* dX, float* dW, void* workspace, size_t workspace_bytes, int32_t* err_flag,

@@ -47,8 +47,8 @@ OrpoLayout make_orpo_layout(int64_t n_seq, int64_t seq_len, int64_t H, int64_t V
 size_t ce_layout_bytes(int64_t BT);
 
 // The kernels address one 256-row tile of an operand (or of the chunk
-// buffer, or of the transposed token chunk) through 32-bit byte offsets
-// below 2^31: false if a tile of these sizes would not fit.
+// buffer, of the transposed token chunk, or of the fp32 dW) through 32-bit
+// byte offsets below 2^31: false if a tile of these sizes would not fit.
 bool tiles_fit(const Layout& L, bool chunk_buffer);
 
 // Checks an entry point makes before it touches a device.  Each returns

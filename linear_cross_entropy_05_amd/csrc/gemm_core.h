@@ -34,6 +34,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "flce_host.h"
 
@@ -495,6 +496,31 @@ __device__ __forceinline__ void wait_barrier() {
 
 __device__ __forceinline__ uint32_t mod5(uint32_t x) { return x >= 5 ? x - 5 : x; }
 
+// A main-loop hook that does nothing.  A hook that is active() takes part in
+// the first kStages stages of the loop, which are then unrolled so that the
+// stage number Q is a compile-time constant (accumulator blocks can only be
+// named by constant indices without spilling them): issue<Q>() runs at the
+// start of stage Q, before any of its copies, and apply<Q>(acc) right after
+// its barrier, before its last 16 MFMAs.  The barrier waits for every memory
+// operation of this wave but the eight copies issued after issue<Q>(), so
+// loads issued there have landed when apply runs (their registers must be
+// passed through an empty asm after the barrier, so that the compiler reads
+// them only from there on).  An active hook needs at least kStages + 1
+// stages.
+struct NoHook {
+  static constexpr int kStages = 0;
+  __device__ __forceinline__ bool active() const { return false; }
+  template <int Q>
+  __device__ __forceinline__ void issue() {}
+  template <int Q>
+  __device__ __forceinline__ void apply(f32x16 (&)[4][4]) {}
+};
+
+template <class F, int... Q>
+__device__ __forceinline__ void unroll_stages(F&& f, std::integer_sequence<int, Q...>) {
+  (f(std::integral_constant<int, Q>{}), ...);
+}
+
 // One tile's pass over K.  LDS holds five 32 KiB operand slabs in a ring:
 // stage k's A tile sits in slab 2k mod 5, its B tile in slab 2k + 1 mod 5.
 // While stage k is multiplied, stage k + 1 is in flight or landed, and
@@ -511,9 +537,9 @@ __device__ __forceinline__ uint32_t mod5(uint32_t x) { return x >= 5 ? x - 5 : x
 // step's MFMAs and the B half after eight of them, so no more than 8 (K-
 // contiguous) or 16 (K-major) LDS reads are outstanding at a time.
 // Copies past the last stage read nothing and write zeros into free slabs.
-template <bool kAKMajor, bool kBKMajor>
+template <bool kAKMajor, bool kBKMajor, class Hook>
 __device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, int64_t m0, const Operand<__bf16>& B,
-                                         int64_t n0, int64_t k0, int64_t k1, f32x16 (&acc)[4][4]) {
+                                         int64_t n0, int64_t k0, int64_t k1, f32x16 (&acc)[4][4], Hook& hook) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wy = wave >> 1, wx = wave & 1;
   LoaderT<kAKMajor> la;
@@ -548,8 +574,10 @@ __device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, i
   uint32_t sa = 0;  // slab of A for the current stage
   load_frags<kAKMajor>(la, smem, 0, wy, lane, fa[0]);
   load_frags<kBKMajor>(lb, smem + kSlab, 0, wx, lane, fb[0]);
-  // every iteration of this loop has a next stage; the last stage follows
-  for (int kt = 0; kt + 1 < nk; ++kt) {
+  // one stage with a next stage; Q >= 0: the hook's stage Q (= kt)
+  auto stage = [&](int kt, auto qc) {
+    constexpr int Q = decltype(qc)::value;
+    if constexpr (Q >= 0) hook.template issue<Q>();
     const char* ta = smem + sa * kSlab;
     const char* tb = smem + mod5(sa + 1) * kSlab;
     const bool more = kt + 2 < nk;
@@ -580,6 +608,7 @@ __device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, i
     // all but this stage's eight A copies landed, so stage kt + 1 is in;
     // after the barrier nobody reads stage kt any more
     wait_barrier<kLoads>();
+    if constexpr (Q >= 0) hook.template apply<Q>(acc);
     const uint32_t sn = mod5(sa + 2);
     load_frags<kAKMajor>(la, smem + sn * kSlab, 0, wy, lane, fa[0]);
     load_frags<kBKMajor>(lb, smem + mod5(sn + 1) * kSlab, 0, wx, lane, fb[0]);
@@ -597,7 +626,13 @@ __device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, i
     }
     __builtin_amdgcn_sched_barrier(0);
     sa = sn;
+  };
+  // every stage of these loops has a next stage; the last stage follows
+  int kt = 0;
+  if (hook.active()) {
+    unroll_stages([&](auto qc) { stage(kt++, qc); }, std::make_integer_sequence<int, Hook::kStages>{});
   }
+  for (; kt + 1 < nk; ++kt) stage(kt, std::integral_constant<int, -1>{});
   {
     const char* ta = smem + sa * kSlab;
     const char* tb = smem + mod5(sa + 1) * kSlab;
@@ -620,21 +655,29 @@ __device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, i
 
 }  // namespace pipe
 
-// acc = A[m0:m0+256, k0:k1) * B[n0:n0+256, k0:k1)^T: the direct-to-LDS
-// pipeline for bf16, the register-staged loop for fp32.
 static_assert(kLdsBytes <= pipe::kRingBytes, "LDS");
 constexpr int kGemmLdsBytes = pipe::kRingBytes;
 
 // Tile-order group size (consecutive tile rows walked column by column).
 constexpr int kTileGroup = 8;
 
+// acc = A[m0:m0+256, k0:k1) * B[n0:n0+256, k0:k1)^T: the direct-to-LDS
+// pipeline for bf16, the register-staged loop for fp32.  The hook runs inside
+// the bf16 loop (see pipe::NoHook); the fp32 loop takes none.
+template <typename T, bool kAKMajor, bool kBKMajor, class Hook>
+__device__ __forceinline__ void gemm_mainloop(char* smem, const Operand<T>& A, int64_t m0, const Operand<T>& B,
+                                              int64_t n0, int64_t k0, int64_t k1, f32x16 (&acc)[4][4], Hook& hook) {
+  if constexpr (sizeof(T) == 2)
+    pipe::mainloop<kAKMajor, kBKMajor>(smem, A, m0, B, n0, k0, k1, acc, hook);
+  else
+    mainloop_regstage<T, kAKMajor, kBKMajor>(smem, A, m0, B, n0, k0, k1, acc);
+}
+
 template <typename T, bool kAKMajor, bool kBKMajor>
 __device__ __forceinline__ void gemm_mainloop(char* smem, const Operand<T>& A, int64_t m0, const Operand<T>& B,
                                               int64_t n0, int64_t k0, int64_t k1, f32x16 (&acc)[4][4]) {
-  if constexpr (sizeof(T) == 2)
-    pipe::mainloop<kAKMajor, kBKMajor>(smem, A, m0, B, n0, k0, k1, acc);
-  else
-    mainloop_regstage<T, kAKMajor, kBKMajor>(smem, A, m0, B, n0, k0, k1, acc);
+  pipe::NoHook none;
+  gemm_mainloop<T, kAKMajor, kBKMajor>(smem, A, m0, B, n0, k0, k1, acc, none);
 }
 
 // Tile (tm, tn) of a tm-count x tn-count grid for tile id t, walking groups

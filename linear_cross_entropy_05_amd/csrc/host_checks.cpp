@@ -160,6 +160,8 @@ bool tiles_fit(const Layout& L, bool chunk_buffer) {
   if (rows * L.H * L.esize > kMax) return false;
   if (chunk_buffer && rows * L.ldz * L.esize > kMax) return false;
   if (chunk_buffer && L.dtype == FLCE_BF16 && rows * L.ldxt * 2 > kMax) return false;
+  // the fp32 dW rows of a 256-row tile (read back by the dW product)
+  if (chunk_buffer && rows * L.H * 4 > kMax) return false;
   return true;
 }
 
@@ -258,8 +260,8 @@ const char* flce_status_str(int status) {
     case FLCE_ERR_LAUNCH: return "kernel launch failed";
     case FLCE_ERR_TARGET: return "target outside [0, V) that is not ignore_index";
     case FLCE_ERR_SHAPE:
-      return "unsupported shape (H must be a multiple of 8 for bf16, 4 for fp32; 256 rows of W, of the logits "
-             "chunk and of the transposed token chunk must each fit in 2^31 bytes)";
+      return "unsupported shape (H must be a multiple of 8 for bf16, 4 for fp32; 256 rows of W, of the fp32 dW, of "
+             "the logits chunk and of the transposed token chunk must each fit in 2^31 bytes)";
     case FLCE_ERR_ALIGN: return "misaligned pointer";
     case FLCE_ERR_SCRATCH: return "more rows than the static scratch of the no-allocation entry point holds";
     default: return "unknown status";

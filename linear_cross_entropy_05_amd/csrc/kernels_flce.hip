@@ -476,6 +476,50 @@ __global__ __launch_bounds__(256) void k_transpose_chunk(const uint16_t* __restr
   }
 }
 
+// Main-loop hook of the dW product on chunks after the first: the old dW
+// values of the tile are added into the accumulators during the first 16
+// stages of its K loop, one 32 x 32 block per stage (block (kt % 4, kt / 4)
+// at stage kt), instead of being read back at the end of the tile, where all
+// tiles of a round would wait for them at once.  The sum is the same
+// old + sum of products, accumulated in another order.  Each lane loads the
+// four 16-byte pieces of its block (four consecutive h of one dW row each);
+// rows past V read as zero (buffer range), columns past H land on other dW
+// entries that are read but never stored.
+struct FoldOld {
+  static constexpr int kStages = 16;
+  u32x4 r;         // buffer resource over the tile's rows of dW
+  uint32_t voff;   // bytes to this lane's element of block (0, 0), piece 0
+  uint32_t row32;  // bytes between dW rows 32 apart
+  bool on;         // uniform: a chunk after the first, with > kStages stages
+  f32x4 buf[4];
+
+  __device__ __forceinline__ bool active() const { return on; }
+  // block (Q % 4, Q / 4): rows 32 (Q / 4) + lane % 32, columns 32 (Q % 4) + 8 g + 4 (lane / 32) ..
+  template <int Q>
+  __device__ __forceinline__ void issue() {
+    const uint32_t o = voff + (uint32_t)(Q >> 2) * row32 + (uint32_t)(Q & 3) * 128u;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(buf[g]) : "v"(o + 32u * g), "s"(r) : "memory");
+  }
+  template <int Q>
+  __device__ __forceinline__ void apply(f32x16 (&acc)[4][4]) {
+    // the loads landed at the barrier before this call; route the registers
+    // through an empty asm placed after it, so nothing reads them earlier
+#pragma unroll
+    for (int g = 0; g < 4; ++g) asm volatile("" : "+v"(buf[g]));
+    f32x16& q = acc[Q & 3][Q >> 2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q[4 * g + e] += buf[g][e];
+  }
+};
+
+// Stages the fold above needs: the loop runs stages 0 .. nk - 2 and folds
+// block kt at stage kt, so all 16 blocks need nk >= 17.
+constexpr int kFoldMinStages = FoldOld::kStages + 1;
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char smem[kGemmLdsBytes];
@@ -483,20 +527,28 @@ __global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
   // groups of 4 vocabulary tiles (measured ~1% faster than 8 for this product)
   grouped_tile(xcd_tile(blockIdx.x, a.nvt * a.nht), a.nvt, a.nht, 4, vt, ht);
   const int64_t v0 = vt * kTile, h0 = ht * kTile;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int vlim = (int)(a.V - v0 < kTile ? a.V - v0 : kTile);
+  const int hlim = (int)(a.H - h0 < kTile ? a.H - h0 : kTile);
 
   // X_chunk^T as the A operand (rows h) and G^T as B (columns v): each lane
   // then holds four consecutive h of one dW row
   f32x16 acc[4][4];
-  if constexpr (sizeof(T) == 2)
-    gemm_mainloop<T, false, true>(smem, a.XT, h0, a.G, v0, 0, a.rows, acc);
-  else
+  bool folded = false;
+  if constexpr (sizeof(T) == 2) {
+    FoldOld fold;
+    fold.on = !a.first && (a.rows + pipe::kBK - 1) / pipe::kBK >= kFoldMinStages;
+    fold.r = pipe::rsrc_words(a.dw + v0 * a.H + h0, ((int64_t)vlim * a.H - h0) * 4);
+    fold.voff = (uint32_t)((((wave & 1) * 128 + (lane & 31)) * a.H + (wave >> 1) * 128 + 4 * (lane >> 5)) * 4);
+    fold.row32 = (uint32_t)(32 * a.H * 4);
+    gemm_mainloop<T, false, true>(smem, a.XT, h0, a.G, v0, 0, a.rows, acc, fold);
+    folded = fold.on;
+  } else {
     gemm_mainloop<T, true, true>(smem, a.X, h0, a.G, v0, 0, a.rows, acc);
+  }
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // accumulator (i, j, e): h = h0 + (wave / 2) 128 + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4,
   //                        v = v0 + (wave % 2) 128 + 32 j + lane % 32
-  const int vlim = (int)(a.V - v0 < kTile ? a.V - v0 : kTile);
-  const int hlim = (int)(a.H - h0 < kTile ? a.H - h0 : kTile);
   float* base = a.dw + v0 * a.H + h0;
   const uint32_t H = (uint32_t)a.H;
   // A lane holds 16-byte pieces of one dW row (v), so direct accesses would
@@ -547,7 +599,7 @@ __global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
     }
   };
   f32x4 x[8], y[8];
-  if (a.first) {
+  if (a.first || folded) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       stage(j);

@@ -116,6 +116,8 @@ FWD_BWD_CASES = [
     (dict(V=2_100_000, C=1, wsb=1 << 62), 7),
     # a 256-row tile of W past 2^31 bytes (H = 4.2 M bf16)
     (dict(H=4_200_000, dt=BF16, C=1, wsb=1 << 62), 7),
+    # a 256-row tile of the fp32 dW past 2^31 bytes (H = 2.1 M; its bf16 W tile still fits)
+    (dict(H=2_100_000, dt=BF16, C=1, wsb=1 << 62), 7),
     # the transposed token chunk (bf16 only): chunk of 4.2 M tokens
     (dict(BT=4_200_000, H=8, dt=BF16, C=4_200_000, wsb=1 << 62), 7),
 ]
