@@ -120,6 +120,37 @@ int flce_orpo(const void* X, const void* W, const int64_t* targets, int64_t n_se
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   int32_t* nvalid = reinterpret_cast<int32_t*>(ws + L.off_nvalid);
+  if (L.one_pass) {
+    // chunks of whole pairs: forward, the pairs' terms and token factors, backward
+    const int64_t B = n_seq / 2;
+    char* region = ws + L.off_region;
+    float* rlc = reinterpret_cast<float*>(ws + L.off_rlc);
+    float* wc = reinterpret_cast<float*>(ws + L.off_wc);
+    double* seq = reinterpret_cast<double*>(ws + L.off_seq);
+    double* pair = reinterpret_cast<double*>(ws + L.off_pair);
+    void* xg = ws + L.off_xg;
+    int64_t* yg = reinterpret_cast<int64_t*>(ws + L.off_yg);
+    void* dxc = ws + L.off_dxc;
+    if (flce::launch_count_valid(targets, BT, V, ignore_index, nvalid, err_flag, s) != hipSuccess)
+      return FLCE_ERR_LAUNCH;
+    // valid tokens of the chosen half (its range check repeats the one above)
+    if (flce::launch_count_valid(targets, B * seq_len, V, ignore_index, nvalid + 1, nvalid + 2, s) != hipSuccess)
+      return FLCE_ERR_LAUNCH;
+    for (int64_t p0 = 0; p0 < B; p0 += L.pairs) {
+      const int64_t np = B - p0 < L.pairs ? B - p0 : L.pairs;
+      const int64_t rows = 2 * np * seq_len;
+      if (flce::launch_orpo_gather(X, targets, H, seq_len, B, p0, np, dtype, xg, yg, s) != hipSuccess ||
+          flce::launch_logits_chunk(L.fb, xg, W, yg, ignore_index, 0, rows, region, rlc, s) != hipSuccess ||
+          flce::launch_orpo_chunk_stats(rlc, yg, seq_len, B, p0, np, ignore_index, beta, nvalid + 1, wc, seq_logp, seq,
+                                        pair, s) != hipSuccess ||
+          flce::launch_grad_chunk(L.fb, xg, W, yg, wc, ignore_index, 0, rows, region, dxc, dW, p0 == 0, s) !=
+              hipSuccess ||
+          flce::launch_orpo_scatter(dxc, H, seq_len, B, p0, np, dtype, dX, s) != hipSuccess)
+        return FLCE_ERR_LAUNCH;
+    }
+    if (flce::launch_orpo_final(seq, pair, B, beta, nvalid + 1, loss, s) != hipSuccess) return FLCE_ERR_LAUNCH;
+    return FLCE_OK;
+  }
   float* rl = reinterpret_cast<float*>(ws + L.off_rowloss);
   float* scale = reinterpret_cast<float*>(ws + L.off_scale);
   double* scratch = reinterpret_cast<double*>(ws + L.off_scratch);

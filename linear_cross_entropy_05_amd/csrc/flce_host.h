@@ -34,11 +34,23 @@ Layout make_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int d
 // Forward only: no chunk buffer; off_chunk == off_dxpart == total.
 Layout make_fwd_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);
 
-// Workspace of flce_orpo: per-token arrays and per-sequence sums, then one
-// region that the forward-only pass and then the fused pass reuse.
+// Workspace of flce_orpo.  One pass when a chunk can hold at least one
+// whole (chosen, rejected) pair: chunks of `pairs` pairs (Cp = 2 pairs
+// seq_len tokens) gathered into contiguous rows, each run forward, then its
+// pair terms and token factors, then backward.  Otherwise two passes over
+// the whole batch: forward only (token losses), sequence terms, then the
+// fused pass with the token factors.
 struct OrpoLayout {
-  size_t off_nvalid, off_rowloss, off_scale, off_scratch, off_region, total;
-  Layout fwd, fb;
+  bool one_pass;
+  int64_t pairs, Cp;
+  size_t off_nvalid;  // int32 [0] N, [1] valid chosen tokens, [2] error flag of the second count
+  // two passes
+  size_t off_rowloss, off_scale, off_scratch;
+  // one pass: chunk token losses and factors, 3 n_seq + B doubles, gathered
+  // rows, targets and dX rows
+  size_t off_rlc, off_wc, off_seq, off_pair, off_xg, off_yg, off_dxc;
+  size_t off_region, total;
+  Layout fwd, fb;  // two passes: both; one pass: fb is the chunk's layout
 };
 OrpoLayout make_orpo_layout(int64_t n_seq, int64_t seq_len, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);
 

@@ -136,19 +136,47 @@ Layout make_fwd_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, i
 OrpoLayout make_orpo_layout(int64_t n_seq, int64_t seq_len, int64_t H, int64_t V, int64_t chunk_tokens, int dtype) {
   OrpoLayout L{};
   const int64_t BT = n_seq * seq_len;
-  L.fwd = make_fwd_layout(BT, H, V, chunk_tokens, dtype);
-  L.fb = make_layout(BT, H, V, chunk_tokens, dtype);
+  const int64_t B = n_seq / 2;
+  // the chunk size fused linear + cross-entropy would take for this batch
+  const int64_t C = make_layout(BT, H, V, chunk_tokens, dtype).C;
+  L.pairs = C / (2 * seq_len);
+  if (L.pairs > B) L.pairs = B;
+  L.one_pass = L.pairs >= 1;
   size_t o = 0;
   L.off_nvalid = o;
   o = align256(o + 16);
-  L.off_rowloss = o;
-  o = align256(o + (size_t)BT * 4);
-  L.off_scale = o;
-  o = align256(o + (size_t)BT * 4);
-  L.off_scratch = o;
-  o = align256(o + (size_t)n_seq * 3 * 8);
-  L.off_region = o;
-  L.total = o + (L.fwd.total > L.fb.total ? L.fwd.total : L.fb.total);
+  if (L.one_pass) {
+    const int64_t esize = dtype == FLCE_BF16 ? 2 : 4;
+    L.Cp = 2 * L.pairs * seq_len;
+    L.fb = make_layout(L.Cp, H, V, L.Cp, dtype);
+    L.off_rlc = o;
+    o = align256(o + (size_t)L.Cp * 4);
+    L.off_wc = o;
+    o = align256(o + (size_t)L.Cp * 4);
+    L.off_seq = o;
+    o = align256(o + (size_t)n_seq * 3 * 8);
+    L.off_pair = o;
+    o = align256(o + (size_t)(B > 0 ? B : 1) * 8);
+    L.off_xg = o;
+    o = align256(o + (size_t)L.Cp * H * esize);
+    L.off_yg = o;
+    o = align256(o + (size_t)L.Cp * 8);
+    L.off_dxc = o;
+    o = align256(o + (size_t)L.Cp * H * esize);
+    L.off_region = o;
+    L.total = o + L.fb.total;
+  } else {
+    L.fwd = make_fwd_layout(BT, H, V, chunk_tokens, dtype);
+    L.fb = make_layout(BT, H, V, chunk_tokens, dtype);
+    L.off_rowloss = o;
+    o = align256(o + (size_t)BT * 4);
+    L.off_scale = o;
+    o = align256(o + (size_t)BT * 4);
+    L.off_scratch = o;
+    o = align256(o + (size_t)n_seq * 3 * 8);
+    L.off_region = o;
+    L.total = o + (L.fwd.total > L.fb.total ? L.fwd.total : L.fb.total);
+  }
   return L;
 }
 
@@ -217,7 +245,7 @@ int check_orpo(const void* X, const void* W, const int64_t* targets, int64_t n_s
       !aligned(dX, 16) || (seq_logp && !aligned(seq_logp, 4)))
     return FLCE_ERR_ALIGN;
   const OrpoLayout L = make_orpo_layout(n_seq, seq_len, H, V, chunk_tokens, dtype);
-  if (!tiles_fit(L.fb, true) || !tiles_fit(L.fwd, false)) return FLCE_ERR_SHAPE;
+  if (!tiles_fit(L.fb, true) || (!L.one_pass && !tiles_fit(L.fwd, false))) return FLCE_ERR_SHAPE;
   if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE;
   *out = L;
   return FLCE_OK;

@@ -701,9 +701,24 @@ static void logits_lse(const Layout& L, const T* X, const T* W, const int64_t* y
 }
 
 template <typename T>
+static hipError_t backward_impl(const Layout& L, const T* X, const T* W, const int64_t* y, const float* scale,
+                                int64_t ign, int64_t c0, int64_t rows, char* ws, T* dX, float* dW, bool first,
+                                hipStream_t s);
+
+template <typename T>
 static hipError_t chunk_impl(const Layout& L, const T* X, const T* W, const int64_t* y, const float* scale,
                              int64_t ign, int64_t c0, int64_t rows, char* ws, float* rowloss, T* dX, float* dW,
                              bool first, hipStream_t s) {
+  logits_lse<T>(L, X, W, y, ign, c0, rows, ws, rowloss, reinterpret_cast<T*>(ws + L.off_chunk), s);
+  return backward_impl<T>(L, X, W, y, scale, ign, c0, rows, ws, dX, dW, first, s);
+}
+
+// The backward half of a chunk whose logits (z - M_h) and statistics are in
+// the workspace: in-place gradient, dX rows, dW (+)=.
+template <typename T>
+static hipError_t backward_impl(const Layout& L, const T* X, const T* W, const int64_t* y, const float* scale,
+                                int64_t ign, int64_t c0, int64_t rows, char* ws, T* dX, float* dW, bool first,
+                                hipStream_t s) {
   const int64_t H = L.H, V = L.V;
   T* z = reinterpret_cast<T*>(ws + L.off_chunk);
   float2* part = reinterpret_cast<float2*>(ws + L.off_part);
@@ -711,8 +726,6 @@ static hipError_t chunk_impl(const Layout& L, const T* X, const T* W, const int6
   const int32_t* nvalid = reinterpret_cast<const int32_t*>(ws + L.off_nvalid);
   const T* Xc = X + c0 * H;
   const int64_t* yc = y + c0;
-
-  logits_lse<T>(L, X, W, y, ign, c0, rows, ws, rowloss, z, s);
   {
     ProfScope ps(kPhaseGrad, s);
     hipLaunchKernelGGL(k_grad<T>, dim3((unsigned)rows), dim3(kGradThreads), 0, s, z, L.ldz, V, lse, part, 2 * L.nvt, yc, ign,
@@ -778,6 +791,27 @@ hipError_t launch_fwd_chunk(const Layout& L, const void* X, const void* W, const
     logits_lse<float>(L, static_cast<const float*>(X), static_cast<const float*>(W), y, ign, c0, rows, ws, rowloss,
                       nullptr, s);
   return hipGetLastError();
+}
+
+hipError_t launch_logits_chunk(const Layout& L, const void* X, const void* W, const int64_t* y, int64_t ign, int64_t c0,
+                               int64_t rows, char* ws, float* rowloss, hipStream_t s) {
+  if (L.dtype == 1)
+    logits_lse<__bf16>(L, static_cast<const __bf16*>(X), static_cast<const __bf16*>(W), y, ign, c0, rows, ws, rowloss,
+                       reinterpret_cast<__bf16*>(ws + L.off_chunk), s);
+  else
+    logits_lse<float>(L, static_cast<const float*>(X), static_cast<const float*>(W), y, ign, c0, rows, ws, rowloss,
+                      reinterpret_cast<float*>(ws + L.off_chunk), s);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_chunk(const Layout& L, const void* X, const void* W, const int64_t* y, const float* scale,
+                             int64_t ign, int64_t c0, int64_t rows, char* ws, void* dX, float* dW, bool first,
+                             hipStream_t s) {
+  if (L.dtype == 1)
+    return backward_impl<__bf16>(L, static_cast<const __bf16*>(X), static_cast<const __bf16*>(W), y, scale, ign, c0,
+                                 rows, ws, static_cast<__bf16*>(dX), dW, first, s);
+  return backward_impl<float>(L, static_cast<const float*>(X), static_cast<const float*>(W), y, scale, ign, c0, rows,
+                              ws, static_cast<float*>(dX), dW, first, s);
 }
 
 hipError_t launch_flce_chunk(const Layout& L, const void* X, const void* W, const int64_t* y, const float* scale,

@@ -106,12 +106,26 @@ int main() {
     } else if (!strcmp(op, "layout") && sscanf(line, "%*s %lld %lld %lld %lld %d", &BT, &H, &V, &C, &dt) == 5) {
       std::string r = check_layout(flce::make_layout(BT, H, V, C, dt), BT, H, V, C);
       if (r == "ok") r = check_fwd_layout(flce::make_fwd_layout(BT, H, V, C, dt), BT);
-      if (r == "ok" && BT >= 2 && BT % 2 == 0) {
-        const flce::OrpoLayout O = flce::make_orpo_layout(2, BT / 2, H, V, C, dt);
-        const size_t region = O.fwd.total > O.fb.total ? O.fwd.total : O.fb.total;
-        if (O.off_region + region != O.total || !a256(O.off_region) ||
-            O.off_scale + (size_t)BT * 4 > O.off_scratch || O.off_rowloss + (size_t)BT * 4 > O.off_scale)
-          r = "orpo layout";
+      for (int ns = 2; r == "ok" && ns <= 8; ns += 6) {
+        if (BT < ns || BT % ns) continue;
+        const int64_t T = BT / ns, B = ns / 2;
+        const flce::OrpoLayout O = flce::make_orpo_layout(ns, T, H, V, C, dt);
+        if (O.one_pass) {
+          const size_t es = dt == 1 ? 2 : 4;
+          if (O.pairs < 1 || O.pairs > B || O.Cp != 2 * O.pairs * T || O.Cp > flce::make_layout(BT, H, V, C, dt).C)
+            r = "orpo pairs per chunk";
+          else if (O.off_nvalid + 12 > O.off_rlc || O.off_rlc + (size_t)O.Cp * 4 > O.off_wc ||
+                   O.off_wc + (size_t)O.Cp * 4 > O.off_seq || O.off_seq + (size_t)ns * 24 > O.off_pair ||
+                   O.off_pair + (size_t)B * 8 > O.off_xg || O.off_xg + (size_t)O.Cp * H * es > O.off_yg ||
+                   O.off_yg + (size_t)O.Cp * 8 > O.off_dxc || O.off_dxc + (size_t)O.Cp * H * es > O.off_region ||
+                   O.off_region + O.fb.total != O.total || !a256(O.off_region) || O.fb.C != O.Cp)
+            r = "orpo one-pass layout";
+        } else {
+          const size_t region = O.fwd.total > O.fb.total ? O.fwd.total : O.fb.total;
+          if (O.off_region + region != O.total || !a256(O.off_region) ||
+              O.off_scale + (size_t)BT * 4 > O.off_scratch || O.off_rowloss + (size_t)BT * 4 > O.off_scale)
+            r = "orpo layout";
+        }
       }
       if (r == "ok" && flce_workspace_bytes(BT, H, V, C, dt) != (BT < 0 ? 0 : flce::make_layout(BT, H, V, C, dt).total))
         r = "workspace query";

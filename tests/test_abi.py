@@ -277,9 +277,17 @@ def test_orpo_host_argument_checks(lib, kw, status):
 
 
 def test_orpo_workspace(lib):
-    # the larger of the two passes' workspaces plus per-token and per-sequence arrays
+    # one pass (a 4096-token chunk holds 2 pairs of 1024-token sequences): one
+    # chunk's workspace, the gathered rows and their dX rows (4096 x 4096 bf16
+    # each), targets, token arrays, per-sequence and per-pair sums
     ws = lib.flce_orpo_workspace_bytes(8, 1024, 4096, 128256, 0, BF16)
+    one = lib.flce_workspace_bytes(4096, 4096, 128256, 4096, BF16)
+    rows = 2 * 4096 * 4096 * 2
+    assert one + rows < ws <= one + rows + 4096 * (8 + 4 + 4) + 8 * 24 + 4 * 8 + 8 * 256
+    # two passes (a 4096-token sequence pair does not fit a 4096-token chunk):
+    # the larger of the two passes' workspaces plus per-token and per-sequence arrays
+    ws2 = lib.flce_orpo_workspace_bytes(2, 4096, 4096, 128256, 0, BF16)
     fb = lib.flce_workspace_bytes(8192, 4096, 128256, 0, BF16)
-    assert fb < ws <= fb + 8192 * 8 + 8 * 24 + 4096
+    assert fb < ws2 <= fb + 8192 * 8 + 2 * 24 + 4096
     assert lib.flce_orpo_workspace_bytes(3, 1024, 4096, 128256, 0, BF16) == 0
     assert lib.flce_orpo_workspace_bytes(8, 0, 4096, 128256, 0, BF16) == 0

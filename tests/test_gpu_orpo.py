@@ -58,6 +58,37 @@ def test_orpo_bf16_chunked_with_empty_sequence():
     _run(4, 160, 136, 700, "bf16", seed=73, beta=0.5, chunk=200, ignore_seq=3)
 
 
+def test_orpo_one_pass_several_chunks_ragged():
+    # 5 pairs of 96-token sequences, chunks of 400 tokens: 2 pairs per chunk,
+    # so three chunks, the last with one pair; the rejected sequence of pair 3
+    # has no valid token
+    _run(10, 96, 136, 700, "bf16", seed=77, beta=0.3, chunk=400, ignore_seq=8)
+
+
+def test_orpo_one_pass_fp32_several_chunks():
+    # 3 pairs, 2 per 160-token chunk
+    _run(6, 40, 64, 300, "fp32", seed=78, chunk=160)
+
+
+def test_orpo_one_and_two_pass_agree():
+    """The same inputs through chunks of whole pairs (one pass) and through
+    chunks too short for a pair (forward pass, sequence terms, fused pass)."""
+    import linear_cross_entropy_05_amd as flce
+
+    n_seq, T, H, V = 4, 60, 72, 500
+    w, X, W, y = _inputs(n_seq, T, H, V, "fp32", seed=79)
+    dev = torch.device("cuda", 0)
+    args = (X.to(dev), W.to(dev), y.to(dev).view(n_seq, T), 0.2, w.ignore_index)
+    one = flce.flce_orpo(*args, 0, seq_logp=True)    # a 240-token chunk holds both pairs
+    two = flce.flce_orpo(*args, 100, seq_logp=True)  # a pair needs 120 tokens
+    torch.cuda.synchronize()
+    assert flce.flce_orpo_workspace_bytes(n_seq, T, H, V, 0, torch.float32) != \
+        flce.flce_orpo_workspace_bytes(n_seq, T, H, V, 100, torch.float32)
+    assert abs(one[0].item() - two[0].item()) <= 1e-6 * abs(two[0].item())
+    assert torch.equal(one[3], two[3])  # sequence scores from the same token losses, same order
+    assert rel_err(to_np(one[1]), to_np(two[1])) <= 1e-5 and rel_err(to_np(one[2]), to_np(two[2])) <= 1e-5
+
+
 def test_orpo_beta_zero_is_chosen_cross_entropy():
     import linear_cross_entropy_05_amd as flce
 
