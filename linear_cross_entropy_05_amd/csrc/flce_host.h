@@ -28,6 +28,9 @@ struct Layout {
   // X_c^T shares the statistics region (off_part): the statistics are dead
   // once the gradient pass has run, and X_c^T is only read by the dW product
   size_t off_nvalid, off_lse, off_rowloss, off_part, off_chunk, off_dxpart, total;
+  // eight int32 tile-queue counters of the logits and dW products (zeroed
+  // before each launch), inside the 256 bytes that start at off_nvalid
+  size_t off_queue;
 };
 
 Layout make_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);
@@ -60,7 +63,8 @@ size_t ce_layout_bytes(int64_t BT);
 
 // The kernels address one 256-row tile of an operand (or of the chunk
 // buffer, of the transposed token chunk, or of the fp32 dW) through 32-bit
-// byte offsets below 2^31: false if a tile of these sizes would not fit.
+// byte offsets below 2^31, and number a launch's tiles with 32-bit ids
+// (at most 2^30 tiles): false if these sizes would not fit.
 bool tiles_fit(const Layout& L, bool chunk_buffer);
 
 // Checks an entry point makes before it touches a device.  Each returns

@@ -79,7 +79,8 @@ Layout make_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int d
   L.splits = pick_splits(tiles, (V + ks - 1) / ks, (size_t)C * H * 4, chunk_bytes);
   size_t o = 0;
   L.off_nvalid = o;
-  o = align256(o + 16);
+  L.off_queue = o + 64;
+  o = align256(o + 96);
   L.off_lse = o;
   o = align256(o + (size_t)C * 4);
   L.off_rowloss = o;
@@ -120,7 +121,8 @@ Layout make_fwd_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, i
   L.splits = 1;
   size_t o = 0;
   L.off_nvalid = o;
-  o = align256(o + 16);
+  L.off_queue = o + 64;
+  o = align256(o + 96);
   L.off_lse = o;
   o = align256(o + (size_t)C * 4);
   L.off_rowloss = o;
@@ -190,6 +192,9 @@ bool tiles_fit(const Layout& L, bool chunk_buffer) {
   if (chunk_buffer && L.dtype == FLCE_BF16 && rows * L.ldxt * 2 > kMax) return false;
   // the fp32 dW rows of a 256-row tile (read back by the dW product)
   if (chunk_buffer && rows * L.H * 4 > kMax) return false;
+  // tile ids of one launch (int32, with room for the launch's extra workgroups)
+  const int64_t ct = (L.C + kTile - 1) / kTile, ht = (L.H + kTile - 1) / kTile;
+  if (L.nvt * ct > (1 << 30) || (chunk_buffer && L.nvt * ht > (1 << 30))) return false;
   return true;
 }
 

@@ -83,6 +83,11 @@ __global__ __launch_bounds__(1024) void k_count_valid(const int64_t* __restrict_
   }
 }
 
+// Counters of a tile queue (TileQueue in gemm_core.h) back to zero before a launch.
+__global__ void k_queue_reset(int* head) {
+  if (threadIdx.x < kXcds) head[threadIdx.x] = 0;
+}
+
 __global__ void k_fill_zero(float* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     p[i] = 0.f;
@@ -98,6 +103,7 @@ struct LogitsArgs {
   int64_t nvh;     // 128-wide vocabulary half tiles: 2 nvt
   T* z;            // chunk buffer [rows, ldz]
   float2* part;    // [rows, nvh] (max, sum of exp) per half tile
+  TileQueue queue; // over nvt x nct tiles
 };
 
 __device__ __forceinline__ void store4(Rsrc r, uint32_t off, float a, float b, float c, float d, __bf16*) {
@@ -137,8 +143,10 @@ constexpr int kNonTemporal = 2;
 template <typename T>
 __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char smem[kGemmLdsBytes];
+  const int tile = take_tile(a.queue, smem);
+  if (tile < 0) return;
   int64_t vt, ct;
-  grouped_tile(xcd_tile(blockIdx.x, a.nvt * a.nct), a.nvt, a.nct, kTileGroup, vt, ct);
+  grouped_tile(tile, a.nvt, a.nct, kTileGroup, vt, ct);
   const int64_t v0 = vt * kTile, c0 = ct * kTile;
 
   f32x16 acc[4][4];
@@ -453,6 +461,7 @@ struct DwArgs {
   int64_t V, H, rows, nvt, nht;
   float* dw;      // [V, H]
   int first;
+  TileQueue queue;  // over nvt x nht tiles
 };
 
 // X_c^T[h][c] = X_c[c][h] for c < rows, 0 for rows <= c < ldxt (the K tail
@@ -523,9 +532,11 @@ constexpr int kFoldMinStages = FoldOld::kStages + 1;
 template <typename T>
 __global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char smem[kGemmLdsBytes];
+  const int tile = take_tile(a.queue, smem);
+  if (tile < 0) return;
   int64_t vt, ht;
   // groups of 4 vocabulary tiles (measured ~1% faster than 8 for this product)
-  grouped_tile(xcd_tile(blockIdx.x, a.nvt * a.nht), a.nvt, a.nht, 4, vt, ht);
+  grouped_tile(tile, a.nvt, a.nht, 4, vt, ht);
   const int64_t v0 = vt * kTile, h0 = ht * kTile;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int vlim = (int)(a.V - v0 < kTile ? a.V - v0 : kTile);
@@ -688,9 +699,11 @@ static void logits_lse(const Layout& L, const T* X, const T* W, const int64_t* y
   la.ldz = L.ldz;
   la.z = z;
   la.part = part;
+  la.queue = TileQueue{reinterpret_cast<int*>(ws + L.off_queue), (int)(la.nvt * la.nct)};
   {
     ProfScope ps(kPhaseLogits, s);
-    hipLaunchKernelGGL(k_logits<T>, dim3((unsigned)(la.nvt * la.nct)), dim3(kThreads), 0, s, la);
+    hipLaunchKernelGGL(k_queue_reset, dim3(1), dim3(64), 0, s, la.queue.head);
+    hipLaunchKernelGGL(k_logits<T>, dim3((unsigned)queue_grid(la.queue.total)), dim3(kThreads), 0, s, la);
   }
 
   {
@@ -772,12 +785,14 @@ static hipError_t backward_impl(const Layout& L, const T* X, const T* W, const i
   wa.nht = (H + kTile - 1) / kTile;
   wa.dw = dW;
   wa.first = first ? 1 : 0;
+  wa.queue = TileQueue{reinterpret_cast<int*>(ws + L.off_queue), (int)(wa.nvt * wa.nht)};
   {
     ProfScope ps(kPhaseDw, s);  // bf16: the chunk transpose is counted with the dW product
     if constexpr (sizeof(T) == 2)
       hipLaunchKernelGGL(k_transpose_chunk, dim3((unsigned)(L.ldxt / 64), (unsigned)((H + 63) / 64)), dim3(256), 0, s,
                          reinterpret_cast<const uint16_t*>(Xc), rows, H, reinterpret_cast<uint16_t*>(xt), L.ldxt);
-    hipLaunchKernelGGL(k_dw<T>, dim3((unsigned)(wa.nvt * wa.nht)), dim3(kThreads), 0, s, wa);
+    hipLaunchKernelGGL(k_queue_reset, dim3(1), dim3(64), 0, s, wa.queue.head);
+    hipLaunchKernelGGL(k_dw<T>, dim3((unsigned)queue_grid(wa.queue.total)), dim3(kThreads), 0, s, wa);
   }
   return hipGetLastError();
 }

@@ -42,7 +42,7 @@ std::string check_layout(const flce::Layout& L, int64_t BT, int64_t H, int64_t V
   const size_t offs[] = {L.off_nvalid, L.off_lse, L.off_rowloss, L.off_part, L.off_chunk, L.off_dxpart, L.total};
   for (size_t o : offs)
     if (!a256(o)) return "unaligned offset";
-  if (L.off_nvalid + 16 > L.off_lse) return "nvalid region";
+  if (L.off_nvalid + 16 > L.off_queue || L.off_queue % 16 || L.off_queue + 32 > L.off_lse) return "nvalid/queue region";
   if (L.off_lse + (size_t)L.C * 4 > L.off_rowloss) return "lse region";
   if (L.off_rowloss + (size_t)(BT > 0 ? BT : 1) * 4 > L.off_part) return "rowloss region";
   const size_t stats = (size_t)L.C * 2 * L.nvt * 8;
@@ -59,6 +59,7 @@ std::string check_fwd_layout(const flce::Layout& L, int64_t BT) {
   for (size_t o : offs)
     if (!a256(o)) return "fwd unaligned offset";
   if (L.C < 1 || (BT > 0 && L.C > BT)) return "fwd pass range";
+  if (L.off_nvalid + 16 > L.off_queue || L.off_queue % 16 || L.off_queue + 32 > L.off_lse) return "fwd nvalid/queue region";
   if (L.off_lse + (size_t)L.C * 4 > L.off_rowloss) return "fwd lse region";
   if (L.off_rowloss + (size_t)(BT > 0 ? BT : 1) * 4 > L.off_part) return "fwd rowloss region";
   if (L.off_part + (size_t)L.C * 2 * L.nvt * 8 > L.total) return "fwd statistics region";
