@@ -486,48 +486,64 @@ __global__ __launch_bounds__(256) void k_transpose_chunk(const uint16_t* __restr
 }
 
 // Main-loop hook of the dW product on chunks after the first: the old dW
-// values of the tile are added into the accumulators during the first 16
-// stages of its K loop, one 32 x 32 block per stage (block (kt % 4, kt / 4)
-// at stage kt), instead of being read back at the end of the tile, where all
-// tiles of a round would wait for them at once.  The sum is the same
-// old + sum of products, accumulated in another order.  Each lane loads the
-// four 16-byte pieces of its block (four consecutive h of one dW row each);
-// rows past V read as zero (buffer range), columns past H land on other dW
-// entries that are read but never stored.
+// values of the tile are added into the accumulators during the first 16 / kPer
+// stages of its K loop, kPer 32 x 32 blocks per stage (blocks kPer kt ..
+// kPer kt + kPer - 1 at stage kt, block b being (b % 4, b / 4)), instead of
+// being read back at the end of the tile, where all tiles of a round would
+// wait for them at once.  The sum is the same old + sum of products,
+// accumulated in another order.  Each lane loads the four 16-byte pieces of
+// each of its blocks (four consecutive h of one dW row each); rows past V read
+// as zero (buffer range), columns past H land on other dW entries that are
+// read but never stored.  One block per stage needs 17 stages (chunks of more
+// than 1024 tokens); two per stage, for shorter chunks, need 9 (measured: two
+// per stage is 0.9% slower on 64-stage tiles, 2.7% faster than the
+// read-modify-write epilogue on 16-stage ones).
+template <int kPer>
 struct FoldOld {
-  static constexpr int kStages = 16;
+  static constexpr int kStages = 16 / kPer;
   u32x4 r;         // buffer resource over the tile's rows of dW
   uint32_t voff;   // bytes to this lane's element of block (0, 0), piece 0
   uint32_t row32;  // bytes between dW rows 32 apart
   bool on;         // uniform: a chunk after the first, with > kStages stages
-  f32x4 buf[4];
+  f32x4 buf[4 * kPer];
 
   __device__ __forceinline__ bool active() const { return on; }
-  // block (Q % 4, Q / 4): rows 32 (Q / 4) + lane % 32, columns 32 (Q % 4) + 8 g + 4 (lane / 32) ..
+  // block b: rows 32 (b / 4) + lane % 32, columns 32 (b % 4) + 8 g + 4 (lane / 32) ..
   template <int Q>
   __device__ __forceinline__ void issue() {
-    const uint32_t o = voff + (uint32_t)(Q >> 2) * row32 + (uint32_t)(Q & 3) * 128u;
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(buf[g]) : "v"(o + 32u * g), "s"(r) : "memory");
+    for (int p = 0; p < kPer; ++p) {
+      const int b = Q * kPer + p;
+      const uint32_t o = voff + (uint32_t)(b >> 2) * row32 + (uint32_t)(b & 3) * 128u;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen"
+                     : "=v"(buf[4 * p + g])
+                     : "v"(o + 32u * g), "s"(r)
+                     : "memory");
+    }
   }
   template <int Q>
   __device__ __forceinline__ void apply(f32x16 (&acc)[4][4]) {
     // the loads landed at the barrier before this call; route the registers
     // through an empty asm placed after it, so nothing reads them earlier
 #pragma unroll
-    for (int g = 0; g < 4; ++g) asm volatile("" : "+v"(buf[g]));
-    f32x16& q = acc[Q & 3][Q >> 2];
+    for (int g = 0; g < 4 * kPer; ++g) asm volatile("" : "+v"(buf[g]));
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+    for (int p = 0; p < kPer; ++p) {
+      f32x16& q = acc[(Q * kPer + p) & 3][(Q * kPer + p) >> 2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) q[4 * g + e] += buf[g][e];
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[4 * g + e] += buf[4 * p + g][e];
+    }
   }
 };
 
-// Stages the fold above needs: the loop runs stages 0 .. nk - 2 and folds
-// block kt at stage kt, so all 16 blocks need nk >= 17.
-constexpr int kFoldMinStages = FoldOld::kStages + 1;
+// The loop runs stages 0 .. nk - 2 with the hook in its first kStages, so a
+// fold needs nk >= kStages + 1.
+template <int kPer>
+constexpr int kFoldMinStages = FoldOld<kPer>::kStages + 1;
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
@@ -547,13 +563,23 @@ __global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
   f32x16 acc[4][4];
   bool folded = false;
   if constexpr (sizeof(T) == 2) {
-    FoldOld fold;
-    fold.on = !a.first && (a.rows + pipe::kBK - 1) / pipe::kBK >= kFoldMinStages;
-    fold.r = pipe::rsrc_words(a.dw + v0 * a.H + h0, ((int64_t)vlim * a.H - h0) * 4);
-    fold.voff = (uint32_t)((((wave & 1) * 128 + (lane & 31)) * a.H + (wave >> 1) * 128 + 4 * (lane >> 5)) * 4);
-    fold.row32 = (uint32_t)(32 * a.H * 4);
-    gemm_mainloop<T, false, true>(smem, a.XT, h0, a.G, v0, 0, a.rows, acc, fold);
-    folded = fold.on;
+    const int64_t nk = (a.rows + pipe::kBK - 1) / pipe::kBK;
+    auto run = [&](auto& fold) {
+      fold.r = pipe::rsrc_words(a.dw + v0 * a.H + h0, ((int64_t)vlim * a.H - h0) * 4);
+      fold.voff = (uint32_t)((((wave & 1) * 128 + (lane & 31)) * a.H + (wave >> 1) * 128 + 4 * (lane >> 5)) * 4);
+      fold.row32 = (uint32_t)(32 * a.H * 4);
+      gemm_mainloop<T, false, true>(smem, a.XT, h0, a.G, v0, 0, a.rows, acc, fold);
+      folded = fold.on;
+    };
+    if (!a.first && nk >= kFoldMinStages<2> && nk < kFoldMinStages<1>) {
+      FoldOld<2> fold;
+      fold.on = true;
+      run(fold);
+    } else {
+      FoldOld<1> fold;
+      fold.on = !a.first && nk >= kFoldMinStages<1>;
+      run(fold);
+    }
   } else {
     gemm_mainloop<T, true, true>(smem, a.X, h0, a.G, v0, 0, a.rows, acc);
   }

@@ -71,22 +71,26 @@ def test_bf16_shape_sweep(BT, H, V, chunk):
     check_against_oracle(si.small(BT, H, V, "bf16", seed=BT + H + V, w_std=0.05), chunk)
 
 
-@pytest.mark.parametrize("BT,H,V,chunk", [(2600, 200, 1000, 1100), (2200, 264, 515, 1088)])
+@pytest.mark.parametrize("BT,H,V,chunk", [(2600, 200, 1000, 1100), (2200, 264, 515, 1088), (2000, 200, 1000, 700),
+                                           (2560, 136, 777, 1024)])
 def test_bf16_long_chunks_fold_old_dw(BT, H, V, chunk):
-    # chunks of >= 1025 tokens (>= 17 K stages of the dW product): on chunks
-    # after the first the old dW rows are added into the accumulators during
-    # the K loop instead of being read back at the end; the ragged last chunk
-    # (400 / 24 tokens) is too short for that and takes the read-modify-write
-    # epilogue; partial vocabulary and hidden tiles in both
+    # on chunks after the first the old dW rows are added into the
+    # accumulators during the K loop of the dW product instead of being read
+    # back at the end: one 32 x 32 block per stage for chunks of >= 1025
+    # tokens (>= 17 K stages: 1100, 1088), two per stage for 513 .. 1024
+    # tokens (9 .. 16 stages: 700 and the ragged 600, 1024); ragged last
+    # chunks too short for either (400 / 24 / 512 tokens) take the
+    # read-modify-write epilogue; partial vocabulary and hidden tiles in all
     check_against_oracle(si.small(BT, H, V, "bf16", seed=BT + V, w_std=0.05), chunk)
 
 
-def test_bf16_long_chunks_deterministic():
-    # the fold path is as deterministic as the store path
+@pytest.mark.parametrize("chunk", [1050, 600])
+def test_bf16_long_chunks_deterministic(chunk):
+    # both fold paths are as deterministic as the store path
     w = si.small(2100, 136, 700, "bf16", seed=29)
     inputs = si.make_inputs(w)
-    a = run_gpu(w, 1050, inputs)[1]
-    b = run_gpu(w, 1050, inputs)[1]
+    a = run_gpu(w, chunk, inputs)[1]
+    b = run_gpu(w, chunk, inputs)[1]
     assert a["loss"] == b["loss"]
     assert torch.equal(a["dX"], b["dX"]) and torch.equal(a["dW"], b["dW"])
 
