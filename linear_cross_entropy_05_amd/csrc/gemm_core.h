@@ -478,6 +478,16 @@ __device__ __forceinline__ void load_frags(const LoaderT<kKMajor>& l, const char
   }
 }
 
+// fragment i of load_frags alone
+template <bool kKMajor>
+__device__ __forceinline__ void load_frag1(const LoaderT<kKMajor>& l, const char* tile, int s, int w, int lane, int i,
+                                           u32x4& f) {
+  if constexpr (kKMajor)
+    f = l.frag(tile, w * 128 + 32 * i, s, lane);
+  else
+    f = l.frag(tile, w * 128 + 32 * i + (lane & 31), 2 * s + (lane >> 5));
+}
+
 // s_waitcnt vmcnt(N): at most N of this wave's copies still in flight
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -570,6 +580,13 @@ __device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, i
   }
   wait_barrier<2 * kLoads>();  // stage 0 is in
 
+  // Where the next step's fragments are read within a step: all four of
+  // an operand at once (A before the step's MFMAs, B after eight of them),
+  // or, when only B is K-major (the dW product), one fragment before each of
+  // MFMAs 0..3 (A) and kSpreadB..kSpreadB+3 (B).  Measured on the three
+  // products: spreading the reads makes dW 1.6% faster and logits 1.1% slower.
+  constexpr bool kSpreadReads = kBKMajor && !kAKMajor;
+  constexpr int kSpreadB = 8;
   u32x4 fa[2][4], fb[2][4];
   uint32_t sa = 0;  // slab of A for the current stage
   load_frags<kAKMajor>(la, smem, 0, wy, lane, fa[0]);
@@ -586,12 +603,21 @@ __device__ __forceinline__ void mainloop(char* smem, const Operand<__bf16>& A, i
     const uint32_t dsta = lds0 + mod5(sa + 4) * kSlab;
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
-      load_frags<kAKMajor>(la, ta, s + 1, wy, lane, fa[(s + 1) & 1]);
+      if constexpr (!kSpreadReads) load_frags<kAKMajor>(la, ta, s + 1, wy, lane, fa[(s + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
       const int nq = s < 2 ? 3 : 2;
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        if (u == 8) {
+        if constexpr (kSpreadReads) {
+          if (u < 4 || (u >= kSpreadB && u < kSpreadB + 4)) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (u < 4)
+              load_frag1<kAKMajor>(la, ta, s + 1, wy, lane, u, fa[(s + 1) & 1][u]);
+            else
+              load_frag1<kBKMajor>(lb, tb, s + 1, wx, lane, u - kSpreadB, fb[(s + 1) & 1][u - kSpreadB]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else if (u == 8) {
           __builtin_amdgcn_sched_barrier(0);
           load_frags<kBKMajor>(lb, tb, s + 1, wx, lane, fb[(s + 1) & 1]);
           __builtin_amdgcn_sched_barrier(0);
