@@ -12,6 +12,26 @@ namespace flce {
 constexpr int kTile = 256;      // output tile edge (M and N) of the MFMA products
 constexpr int kRowBytes = 128;  // K bytes per tile row per pipeline stage
 
+// Tile ranges of a GEMM launch.  Workgroups are dealt round-robin over the
+// chip's kXcds XCDs (workgroup b runs on XCD b % kXcds), and the tile ids
+// [0, total) of a launch are split into kXcds contiguous ranges, one per XCD,
+// so that the tiles an XCD runs at once are neighbours sharing operand blocks
+// in its L2: range x starts at xcd_first(total, x) and holds
+// xcd_len(total, x) tiles.  (constexpr, so also callable from device code.)
+constexpr int kXcds = 8;
+constexpr int64_t xcd_len(int64_t total, int64_t x) { return total / kXcds + (x < total % kXcds ? 1 : 0); }
+constexpr int64_t xcd_first(int64_t total, int64_t x) {
+  return x * (total / kXcds) + (x < total % kXcds ? x : total % kXcds);
+}
+// Static order over a launch of exactly `total` workgroups: workgroup b takes
+// tile k = b / kXcds of its XCD's range (a bijection onto [0, total)).
+constexpr int64_t xcd_tile(int64_t b, int64_t total) { return xcd_first(total, b % kXcds) + b / kXcds; }
+// Workgroups of a launch whose tiles are taken at run time (TileQueue): one
+// eighth more than the tiles, as many for each XCD.
+constexpr int64_t queue_grid(int64_t total) {
+  return kXcds * ((total + kXcds - 1) / kXcds + ((total + kXcds - 1) / kXcds + 7) / 8);
+}
+
 // Workspace of one flce_fwd_bwd call: where each scratch array lives.  The
 // chunk buffer holds one chunk's logits, then (in place) their gradient; it
 // is the only large array.  Offsets are in bytes from the workspace base,

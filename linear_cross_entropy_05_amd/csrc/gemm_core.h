@@ -720,19 +720,9 @@ __device__ __forceinline__ void grouped_tile(int64_t t, int64_t ntm, int64_t ntn
   tn = l / rows;
 }
 
-// Map a linear workgroup id onto a tile id so that each XCD (workgroups are
-// dealt round-robin over 8 of them) walks one contiguous range of tile ids:
-// neighbouring tiles share an operand block, which then stays in that XCD's L2.
-constexpr int kXcds = 8;
-__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t total) {
-  const int64_t x = b % kXcds, k = b / kXcds;
-  const int64_t q = total / kXcds, r = total % kXcds;
-  return x * q + (x < r ? x : r) + k;
-}
-
-// Tiles of one launch handed out at run time.  The tile ids [0, total) are
-// split into the same eight contiguous ranges as xcd_tile's, one per XCD,
-// each with a counter in `head` (zero at launch).  A workgroup takes the next
+// Tiles of one launch handed out at run time.  Each XCD's range of tile ids
+// (xcd_first, xcd_len in flce_host.h) has a counter in `head` (zero at
+// launch).  A workgroup takes the next
 // tile of its XCD's range; once that range is used up, the next tile of
 // another XCD's range.  The XCDs do not run equally fast (a few percent apart
 // on the same tiles), so with tiles fixed per XCD the launch lasts as long as
@@ -746,24 +736,16 @@ struct TileQueue {
   int total;
 };
 
-// Workgroups of a launch over `total` tiles: one eighth more than the tiles,
-// as many for each XCD.
-inline int64_t queue_grid(int64_t total) {
-  const int64_t per = (total + kXcds - 1) / kXcds;
-  return kXcds * (per + (per + 7) / 8);
-}
-
 // The tile this workgroup computes, or -1.  Uses the first bytes of `smem`
 // (free before the main loop) to hand thread 0's answer to the workgroup.
 __device__ __forceinline__ int take_tile(const TileQueue& q, char* smem) {
   if (threadIdx.x == 0) {
-    const int per = q.total / kXcds, rem = q.total % kXcds;
     const int x = (int)(blockIdx.x % kXcds);
     int t = -1;
     for (int i = 0; i < kXcds && t < 0; ++i) {
       const int y = (x + i) % kXcds;
       const int v = atomicAdd(q.head + y, 1);
-      if (v < per + (y < rem ? 1 : 0)) t = y * per + (y < rem ? y : rem) + v;
+      if (v < xcd_len(q.total, y)) t = (int)xcd_first(q.total, y) + v;
     }
     *reinterpret_cast<volatile int*>(smem) = t;
   }

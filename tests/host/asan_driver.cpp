@@ -9,6 +9,8 @@
 //   ce_noalloc lg t BT V loss rl err max_rows             -> status of check_ce_noalloc
 //   layout BT H V C dt                                    -> "ok" or the broken layout invariant
 //   query BT H V C dt                                     -> the size queries of flce.h, comma-separated
+//   tiles N                                               -> "ok" or the broken invariant of the per-XCD tile
+//                                                            ranges, for every launch of 0 .. N tiles
 // Pointers are plain integers (never dereferenced); 0 is a null pointer.
 #include <stdint.h>
 #include <stdio.h>
@@ -64,6 +66,33 @@ std::string check_fwd_layout(const flce::Layout& L, int64_t BT) {
   if (L.off_rowloss + (size_t)(BT > 0 ? BT : 1) * 4 > L.off_part) return "fwd rowloss region";
   if (L.off_part + (size_t)L.C * 2 * L.nvt * 8 > L.total) return "fwd statistics region";
   if (L.off_chunk != L.total || L.off_dxpart != L.total) return "fwd has a chunk";
+  return "ok";
+}
+
+// The per-XCD tile ranges of a launch of `total` tiles partition [0, total)
+// in order, differ in length by at most one, the static order is a bijection,
+// and a queue launch gives every XCD at least as many workgroups as its range.
+std::string check_tiles(int64_t total) {
+  int64_t next = 0, lmin = total, lmax = 0;
+  for (int x = 0; x < flce::kXcds; ++x) {
+    const int64_t f = flce::xcd_first(total, x), l = flce::xcd_len(total, x);
+    if (f != next || l < 0) return "ranges not contiguous";
+    next = f + l;
+    lmin = l < lmin ? l : lmin;
+    lmax = l > lmax ? l : lmax;
+    if (flce::queue_grid(total) / flce::kXcds < l) return "queue grid short";
+  }
+  if (next != total) return "ranges do not cover the launch";
+  if (lmax - lmin > 1) return "ranges unbalanced";
+  if (flce::queue_grid(total) % flce::kXcds) return "queue grid not a multiple of the XCDs";
+  if (total <= 4096) {
+    std::string seen((size_t)total, '0');
+    for (int64_t b = 0; b < total; ++b) {
+      const int64_t t = flce::xcd_tile(b, total);
+      if (t < 0 || t >= total || seen[(size_t)t] != '0') return "static order not a bijection";
+      seen[(size_t)t] = '1';
+    }
+  }
   return "ok";
 }
 
@@ -130,6 +159,12 @@ int main() {
       }
       if (r == "ok" && flce_workspace_bytes(BT, H, V, C, dt) != (BT < 0 ? 0 : flce::make_layout(BT, H, V, C, dt).total))
         r = "workspace query";
+      printf("%s\n", r.c_str());
+    } else if (!strcmp(op, "tiles") && sscanf(line, "%*s %lld", &BT) == 1) {
+      std::string r = "ok";
+      for (int64_t n = 0; n <= BT && r == "ok"; ++n) r = check_tiles(n);
+      for (int64_t n : {(int64_t)8016, (int64_t)16032, (int64_t)(1 << 30) - 1, (int64_t)(1 << 30)})
+        if (r == "ok") r = check_tiles(n);
       printf("%s\n", r.c_str());
     } else if (!strcmp(op, "query") && sscanf(line, "%*s %lld %lld %lld %lld %d", &BT, &H, &V, &C, &dt) == 5) {
       printf("%lld,%zu,%zu,%zu,%zu\n", (long long)flce_chunk_tokens(BT, H, V, C, dt),

@@ -96,3 +96,9 @@ def test_size_queries_reject_huge_sizes_under_sanitizers(driver):
     assert got[:5] == ["0,0,0,0,0", f"0,0,0,0,{256 + 8192 * 4}", "0,0,0,0,0", "0,0,0,0,0", "0,0,0,0,0"], got
     # the largest accepted token count still gives a layout (and no overflow)
     assert all(int(v) > 0 for v in got[5].split(",")[:3]), got[5]
+
+
+def test_xcd_tile_ranges_under_sanitizers(driver):
+    # every launch size up to 20,000 tiles plus the Llama head's and the
+    # largest one the checks allow: the per-XCD ranges partition the tiles
+    assert _run(driver, ["tiles 20000"]) == ["ok"]
