@@ -57,9 +57,12 @@ def test_bf16_ragged_multi_tile():
     check_against_oracle(si.small(700, 200, 1000, "bf16", seed=22, w_std=0.05), 256)
 
 
-def test_bf16_wide_hidden_split_dx():
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_wide_hidden_split_dx(dtype):
     # few token tiles and a long vocabulary: the dX product is split along V
-    check_against_oracle(si.small(300, 520, 5000, "bf16", seed=23), 300)
+    # (9 splits in bf16, 16 in fp32), and the split sum reads the fp32
+    # partials four at a time
+    check_against_oracle(si.small(300, 520, 5000, dtype, seed=23), 300)
 
 
 @pytest.mark.parametrize("BT,H,V,chunk", [(130, 72, 300, 64), (257, 136, 777, 100), (65, 520, 1300, 0),
