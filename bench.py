@@ -46,6 +46,7 @@ def gpu_bench(w, steps, warmup, forward=True):
     log(f"[bench] inputs {w.name}: BT={w.BT} H={w.H} V={w.V} {w.dtype}")
     X, W, y = si.make_inputs(w)
     Xd, Wd, yd = X.to(dev), W.to(dev), y.to(dev)
+    n_valid = int((y != w.ignore_index).sum())  # the tokens the products compute (ignored ones are skipped)
     del X, W
     C = flce.flce_chunk_tokens(w.BT, w.H, w.V, w.chunk_tokens, w.torch_dtype)
     ws_bytes = flce.flce_workspace_bytes(w.BT, w.H, w.V, w.chunk_tokens, w.torch_dtype)
@@ -121,7 +122,8 @@ def gpu_bench(w, steps, warmup, forward=True):
         + ", ".join(f"{k} {v['ms_per_step']:.3f}" for k, v in kernels.items()))
     return {"ms": ms, "ms_min": per_step[0], "ms_median": per_step[len(per_step) // 2], "fwd_ms": fwd_ms,
             "hooked_ms": hooked_ms,
-            "orpo": orpo, "eager": eager, "lib": lib, "C": C, "ws_bytes": ws_bytes, "peak_extra": peak_extra,
+            "orpo": orpo, "eager": eager, "lib": lib, "C": C, "n_valid": n_valid, "ws_bytes": ws_bytes,
+            "peak_extra": peak_extra,
             "loss": loss,
             "kernels": kernels,
             "cus": props.multi_processor_count, "arch": getattr(props, "gcnArchName", "?")}
@@ -235,7 +237,8 @@ def time_library_gemms(w, Xd, Wd, C, stream, reps=5):
     torch.cuda.empty_cache()
     log("[bench] vendor GEMMs per chunk: " + ", ".join(f"{k} {v['ms']:.3f} ms" for k, v in out.items()))
     out["what"] = (f"torch.mm (hipBLASLt) on one {C}-token chunk: X_c W^T, G W, G^T X_c, bf16 outputs; "
-                   "this library's products also compute the softmax statistics (logits) and accumulate dW in fp32")
+                   "this library's products also compute the softmax statistics (logits) and accumulate dW in fp32; "
+                   "its chunks hold only the non-ignored tokens (this_library_tokens_per_launch on average)")
     return out
 
 
@@ -367,16 +370,19 @@ def roofline(w, r):
     name, k = max(r["kernels"].items(), key=lambda kv: kv[1]["ms_per_step"])
     C = r["C"]
     nchunks = -(-w.BT // C)
+    # The chunks hold only the non-ignored tokens (N of them), so the launches
+    # of one call cover N tokens in all: N / nchunks per launch on average.
+    n = r.get("n_valid", w.BT)
     per_launch_flops = {
         # each GEMM launch covers one chunk: 2 * tokens * H * V
-        "logits": 2.0 * w.BT * w.H * w.V / nchunks,
-        "dx": 2.0 * w.BT * w.H * w.V / nchunks,
-        "dw": 2.0 * w.BT * w.H * w.V / nchunks,
+        "logits": 2.0 * n * w.H * w.V / nchunks,
+        "dx": 2.0 * n * w.H * w.V / nchunks,
+        "dw": 2.0 * n * w.H * w.V / nchunks,
     }
     esz = 2 if w.dtype == "bf16" else 4
     per_launch_bytes = {
         # one chunk of logits read + gradient written, in place
-        "grad_inplace": 2.0 * (w.BT / nchunks) * w.V * esz,
+        "grad_inplace": 2.0 * (n / nchunks) * w.V * esz,
     }
     if name in per_launch_flops:
         achieved = per_launch_flops[name] / (k["avg_ms"] * 1e-3) / 1e12
@@ -476,6 +482,10 @@ def main(argv=None):
                    "targets": w.targets},
         "tflops": round(tflops, 2),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        # the same rate counting only the flops the products compute: the
+        # ignored tokens do not enter them (6 N H V instead of 6 BT H V)
+        "tokens_computed": r["n_valid"],
+        "tflops_computed": round(6.0 * r["n_valid"] * w.H * w.V / (r["ms"] * 1e-3) / 1e12, 2),
         "peak_extra_bytes": int(r["peak_extra"]),
         "workspace_bytes": int(r["ws_bytes"]),
         "dominant_kernel": dom,
@@ -488,7 +498,8 @@ def main(argv=None):
         "torch_eager": r["eager"],
         "vendor_gemm_per_chunk": None if r["lib"] is None else dict(
             r["lib"], this_library_ms={k: round(r["kernels"][k]["avg_ms"], 4) for k in ("logits", "dx", "dw")
-                                       if k in r["kernels"]}),
+                                       if k in r["kernels"]},
+            this_library_tokens_per_launch=round(r["n_valid"] / -(-w.BT // r["C"]), 1)),
         "ce_inplace": ce,
         "forward_only": None if r["fwd_ms"] is None else {
             "ms_per_step": round(r["fwd_ms"], 4), "tokens_per_s": round(w.BT / (r["fwd_ms"] * 1e-3), 1),

@@ -81,9 +81,11 @@ int64_t flce_chunk_tokens(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens
  * chunk (chunk x round_up(V, 256) elements of the dtype) plus per-token and
  * per-tile statistics (O(chunk x V / 256) floats; for bf16 the region is at
  * least H x round_up(chunk, 64) x 2 bytes, as it also holds the transposed
- * token chunk for the dW product once the statistics are consumed) and, when
- * the dX product is split along the vocabulary, fp32 partials bounded by half
- * the chunk or 128 MiB, whichever is larger.
+ * token chunk for the dW product once the statistics are consumed), the
+ * chunk's gathered token rows (chunk x H elements, plus 12 bytes per chunk
+ * token and 4 per token of the batch) and, when the dX product is split along
+ * the vocabulary, fp32 partials bounded by half the chunk or 128 MiB,
+ * whichever is larger.
  * This is the whole extra memory of the call.  Returns 0 for invalid args. */
 size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);
 
@@ -106,6 +108,11 @@ size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, int64_t chunk_toke
  *   err_flag device int32: 0, or FLCE_ERR_TARGET after the call completes
  * With token_scale NULL the gradients are for an upstream gradient of 1 on the
  * mean loss; scale them for another.
+ * Only the non-ignored tokens go through the products: they are packed, in
+ * their order, into chunks of chunk tokens (the last ones fewer, or none),
+ * and the ignored tokens' dX rows and losses are written as zeros.  Every
+ * result is the same as with all tokens in the products (ignored rows add
+ * exact zeros), except the grouping of dW's sum over chunks.
  * Size limits (status FLCE_ERR_SHAPE): the kernels address a 256-row tile with
  * 32-bit byte offsets, so 256 * H * esize, 256 * H * 4 (the fp32 dW),
  * 256 * round_up(V, 256) * esize and, for bf16, 256 * round_up(chunk, 64) * 2
@@ -205,8 +212,9 @@ int ce_fwd_bwd_inplace_noalloc(float* logits, const int64_t* targets, int64_t BT
  * launches.  Kinds: 0 target count, 1 logits GEMM + softmax statistics,
  * 2 log-sum-exp, 3 in-place logits gradient, 4 dX GEMM, 5 dX split sum,
  * 6 dW GEMM, 7 final mean, 8 logits-only cross-entropy rows, 9 zero fill,
- * 10 ORPO sequence statistics. */
-#define FLCE_NUM_KERNEL_KINDS 11
+ * 10 ORPO sequence statistics, 11 token compaction (ignored tokens' rows
+ * zeroed, each chunk's rows gathered). */
+#define FLCE_NUM_KERNEL_KINDS 12
 int flce_profile_begin(int max_launches);
 int flce_profile_end(double* total_ms, int64_t* launches, int n);
 

@@ -373,7 +373,7 @@ def ce_noalloc_max_rows() -> int:
 
 
 KERNEL_KINDS = ["count_valid", "logits", "lse", "grad_inplace", "dx", "dx_reduce", "dw", "loss_final",
-                "ce_rows", "fill_zero", "orpo_stats"]
+                "ce_rows", "fill_zero", "orpo_stats", "gather"]
 
 
 class KernelTimer:

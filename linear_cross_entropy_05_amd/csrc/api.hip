@@ -67,8 +67,8 @@ int flce_fwd_bwd(const void* X, const void* W, const int64_t* targets, const flo
   int32_t* nvalid = reinterpret_cast<int32_t*>(ws + L.off_nvalid);
   float* rl = row_loss ? row_loss : reinterpret_cast<float*>(ws + L.off_rowloss);
 
-  if (flce::launch_count_valid(targets, BT, V, ignore_index, nvalid, err_flag, s) != hipSuccess)
-    return FLCE_ERR_LAUNCH;
+  // only the non-ignored tokens go through the chunks, packed in their order
+  if (flce::launch_compact(L, targets, ignore_index, ws, err_flag, dX, rl, s) != hipSuccess) return FLCE_ERR_LAUNCH;
   if (BT == 0) {
     if (flce::launch_fill_zero(dW, V * H, s) != hipSuccess) return FLCE_ERR_LAUNCH;
   }

@@ -51,9 +51,18 @@ struct Layout {
   // eight int32 tile-queue counters of the logits and dW products (zeroed
   // before each launch), inside the 256 bytes that start at off_nvalid
   size_t off_queue;
+  // Token compaction (flce_fwd_bwd): only the non-ignored tokens go through
+  // the chunks, packed in their order.  idx [BT] int32 holds their positions,
+  // then those of the ignored tokens; each chunk's rows of X, targets and
+  // token scales are gathered into xs [C, H], ys [C] int64 and ss [C] fp32.
+  // Without compaction the four offsets are 0 and the regions absent.
+  bool compact;
+  size_t off_idx, off_ys, off_ss, off_xs;
 };
 
-Layout make_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);
+// compact: the layout of flce_fwd_bwd (token compaction); false for the
+// passes that process every token of a chunk (ORPO)
+Layout make_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype, bool compact);
 // Forward only: no chunk buffer; off_chunk == off_dxpart == total.
 Layout make_fwd_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype);
 

@@ -22,6 +22,7 @@ enum Phase {
   kPhaseCeRows,     // logits-only cross-entropy rows
   kPhaseFill,       // zero fill
   kPhaseOrpo,       // ORPO sequence statistics and token gradient factors
+  kPhaseGather,     // token compaction: ignored rows zeroed, chunk rows gathered
   kNumPhases
 };
 
@@ -40,6 +41,14 @@ class ProfScope {
 hipError_t launch_count_valid(const int64_t* y, int64_t BT, int64_t V, int64_t ignore_index, int32_t* nvalid,
                               int32_t* err, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+// Token compaction (a layout with L.compact), once per call before the
+// chunks: N, the target check, the positions of the non-ignored tokens (then
+// the ignored ones) and zeros in the ignored tokens' dX rows and losses.
+hipError_t launch_compact(const Layout& L, const int64_t* y, int64_t ignore_index, char* ws, int32_t* err, void* dX,
+                          float* rowloss, hipStream_t s);
+// One chunk, forward and backward.  Without compaction: tokens c0 .. c0 +
+// rows - 1.  With it (L.compact, after launch_compact): the non-ignored
+// tokens c0 .. c0 + rows - 1 in their order, of which those below N exist.
 // scale: NULL (gradient factor 1/N) or per-token gradient factors [BT]
 hipError_t launch_flce_chunk(const Layout& L, const void* X, const void* W, const int64_t* y, const float* scale,
                              int64_t ignore_index, int64_t c0, int64_t rows, char* ws, float* rowloss, void* dX,

@@ -46,7 +46,7 @@ int64_t pick_splits(int64_t tiles, int64_t kstages, size_t part_bytes_per_split,
 
 }  // namespace
 
-Layout make_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype) {
+Layout make_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype, bool compact) {
   Layout L{};
   L.BT = BT;
   L.H = H;
@@ -85,6 +85,17 @@ Layout make_layout(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int d
   o = align256(o + (size_t)C * 4);
   L.off_rowloss = o;
   o = align256(o + (size_t)(BT > 0 ? BT : 1) * 4);
+  L.compact = compact;
+  if (compact) {
+    L.off_idx = o;
+    o = align256(o + (size_t)(BT > 0 ? BT : 1) * 4);
+    L.off_ys = o;
+    o = align256(o + (size_t)C * 8);
+    L.off_ss = o;
+    o = align256(o + (size_t)C * 4);
+    L.off_xs = o;
+    o = align256(o + (size_t)C * H * L.esize);
+  }
   L.off_part = o;
   L.ldxt = (C + 63) / 64 * 64;
   {
@@ -140,7 +151,7 @@ OrpoLayout make_orpo_layout(int64_t n_seq, int64_t seq_len, int64_t H, int64_t V
   const int64_t BT = n_seq * seq_len;
   const int64_t B = n_seq / 2;
   // the chunk size fused linear + cross-entropy would take for this batch
-  const int64_t C = make_layout(BT, H, V, chunk_tokens, dtype).C;
+  const int64_t C = make_layout(BT, H, V, chunk_tokens, dtype, false).C;
   L.pairs = C / (2 * seq_len);
   if (L.pairs > B) L.pairs = B;
   L.one_pass = L.pairs >= 1;
@@ -150,7 +161,7 @@ OrpoLayout make_orpo_layout(int64_t n_seq, int64_t seq_len, int64_t H, int64_t V
   if (L.one_pass) {
     const int64_t esize = dtype == FLCE_BF16 ? 2 : 4;
     L.Cp = 2 * L.pairs * seq_len;
-    L.fb = make_layout(L.Cp, H, V, L.Cp, dtype);
+    L.fb = make_layout(L.Cp, H, V, L.Cp, dtype, false);
     L.off_rlc = o;
     o = align256(o + (size_t)L.Cp * 4);
     L.off_wc = o;
@@ -169,7 +180,7 @@ OrpoLayout make_orpo_layout(int64_t n_seq, int64_t seq_len, int64_t H, int64_t V
     L.total = o + L.fb.total;
   } else {
     L.fwd = make_fwd_layout(BT, H, V, chunk_tokens, dtype);
-    L.fb = make_layout(BT, H, V, chunk_tokens, dtype);
+    L.fb = make_layout(BT, H, V, chunk_tokens, dtype, false);
     L.off_rowloss = o;
     o = align256(o + (size_t)BT * 4);
     L.off_scale = o;
@@ -211,7 +222,7 @@ int check_fwd_bwd(const void* X, const void* W, const int64_t* targets, const fl
       !aligned(dW, 16) || (dX && !aligned(dX, 16)) || (row_loss && !aligned(row_loss, 4)) ||
       (token_scale && !aligned(token_scale, 4)))
     return FLCE_ERR_ALIGN;
-  const Layout L = make_layout(BT, H, V, chunk_tokens, dtype);
+  const Layout L = make_layout(BT, H, V, chunk_tokens, dtype, true);
   if (!tiles_fit(L, true)) return FLCE_ERR_SHAPE;
   if (workspace_bytes < L.total) return FLCE_ERR_WORKSPACE;
   *out = L;
@@ -303,12 +314,12 @@ const char* flce_status_str(int status) {
 
 int64_t flce_chunk_tokens(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype) {
   if (!flce::sizes_ok(BT, H, V) || !flce::dtype_ok(dtype)) return 0;
-  return flce::make_layout(BT, H, V, chunk_tokens, dtype).C;
+  return flce::make_layout(BT, H, V, chunk_tokens, dtype, true).C;
 }
 
 size_t flce_workspace_bytes(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype) {
   if (!flce::sizes_ok(BT, H, V) || !flce::dtype_ok(dtype)) return 0;
-  return flce::make_layout(BT, H, V, chunk_tokens, dtype).total;
+  return flce::make_layout(BT, H, V, chunk_tokens, dtype, true).total;
 }
 
 size_t flce_fwd_workspace_bytes(int64_t BT, int64_t H, int64_t V, int64_t chunk_tokens, int dtype) {

@@ -50,36 +50,129 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // ---- count valid targets, range check (once per call) ----------------------
 
+// N = number of targets that are not ignore_index, and error 6 if one of them
+// lies outside [0, V).  With `idx` (token compaction) also the positions:
+// the non-ignored tokens' in order at idx[0 .. N), the ignored tokens' from
+// the end backwards (the j-th ignored position at idx[BT - 1 - j]).  One
+// workgroup, 4096 targets per pass, four consecutive ones per thread, ranks
+// from a scan over the threads in order.
 __global__ __launch_bounds__(1024) void k_count_valid(const int64_t* __restrict__ y, int64_t BT, int64_t V,
-                                                      int64_t ign, int32_t* nvalid, int32_t* err) {
-  __shared__ int red_n[16], red_b[16];
-  int n = 0, bad = 0;
-  for (int64_t i = threadIdx.x; i < BT; i += 1024) {
-    const int64_t t = y[i];
-    if (t != ign) {
-      ++n;
-      bad |= (t < 0 || t >= V);
+                                                      int64_t ign, int32_t* nvalid, int32_t* err,
+                                                      int32_t* __restrict__ idx) {
+  __shared__ int wtot[16], red_b[16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int bad = 0;
+  int64_t done = 0;  // non-ignored targets before this pass
+  for (int64_t base = 0; base < BT; base += 4096) {
+    const int64_t i0 = base + 4 * (int64_t)threadIdx.x;
+    bool f[4];
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f[q] = false;
+      if (i0 + q < BT) {
+        const int64_t t = y[i0 + q];
+        if (t != ign) {
+          f[q] = true;
+          bad |= (t < 0 || t >= V);
+        }
+      }
+      cnt += f[q];
     }
+    // inclusive scan of cnt over the lanes, then over the waves
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o);
+      if (lane >= o) incl += u;
+    }
+    if (lane == 63) wtot[w] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int u = wtot[k];
+      before += k < w ? u : 0;
+      total += u;
+    }
+    __syncthreads();  // wtot is written again by the next pass
+    if (idx) {
+      int64_t r = done + before + incl - cnt;  // non-ignored targets before i0
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t i = i0 + q;
+        if (i < BT) {
+          if (f[q])
+            idx[r++] = (int32_t)i;
+          else
+            idx[BT - 1 - (i - r)] = (int32_t)i;  // i - r ignored targets before i
+        }
+      }
+    }
+    done += total;
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    n += __shfl_xor(n, o);
-    bad |= __shfl_xor(bad, o);
-  }
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    red_n[w] = n;
-    red_b[w] = bad;
-  }
+  for (int o = 32; o > 0; o >>= 1) bad |= __shfl_xor(bad, o);
+  if (lane == 0) red_b[w] = bad;
   __syncthreads();
   if (threadIdx.x == 0) {
-    int tn = 0, tb = 0;
-    for (int i = 0; i < 16; ++i) {
-      tn += red_n[i];
-      tb |= red_b[i];
-    }
-    *nvalid = tn;
+    int tb = 0;
+    for (int i = 0; i < 16; ++i) tb |= red_b[i];
+    *nvalid = (int32_t)done;
     *err = tb ? 6 : 0;
+  }
+}
+
+// Rows of a chunk.  With token compaction a chunk holds the non-ignored
+// tokens c0 .. c0 + max - 1 of the N in device memory, so fewer rows (or
+// none) may be in use; otherwise all `max` are.
+struct RowCount {
+  const int32_t* n;  // N, or nullptr: all max rows
+  int64_t c0, max;
+  __device__ __forceinline__ int64_t get() const {
+    if (!n) return max;
+    const int64_t r = (int64_t)__builtin_amdgcn_readfirstlane(*n) - c0;
+    return r < 0 ? 0 : (r > max ? max : r);
+  }
+};
+
+// Token compaction, once per call: zero the dX rows and token losses of the
+// ignored tokens (idx[N .. BT)), which no chunk visits.
+template <typename T>
+__global__ __launch_bounds__(256) void k_zero_ignored(const int32_t* __restrict__ idx, const int32_t* __restrict__ nvalid,
+                                                      int64_t BT, int64_t H, T* __restrict__ dX,
+                                                      float* __restrict__ rowloss) {
+  constexpr int E = Elem<T>::chunk;
+  const int64_t n = __builtin_amdgcn_readfirstlane(*nvalid);
+  for (int64_t r = n + blockIdx.x; r < BT; r += gridDim.x) {
+    const int64_t p = idx[r];
+    T* row = dX + p * H;
+    for (int64_t h = (int64_t)threadIdx.x * E; h < H; h += 256 * E)
+      *reinterpret_cast<u32x4*>(row + h) = u32x4{0, 0, 0, 0};
+    if (threadIdx.x == 0) rowloss[p] = 0.f;
+  }
+}
+
+// Token compaction, per chunk: row r of the chunk is token idx[c0 + r]; copy
+// its X row, target and token scale into contiguous arrays.
+template <typename T>
+__global__ __launch_bounds__(256) void k_gather_chunk(const T* __restrict__ X, const int64_t* __restrict__ y,
+                                                      const float* __restrict__ scale, int64_t H,
+                                                      const int32_t* __restrict__ idx, RowCount rc,
+                                                      T* __restrict__ xs, int64_t* __restrict__ ys,
+                                                      float* __restrict__ ss) {
+  constexpr int E = Elem<T>::chunk;
+  const int64_t rows = rc.get();
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const int64_t p = idx[rc.c0 + r];
+    const T* src = X + p * H;
+    T* dst = xs + r * H;
+    for (int64_t h = (int64_t)threadIdx.x * E; h < H; h += 256 * E)
+      *reinterpret_cast<u32x4*>(dst + h) = *reinterpret_cast<const u32x4*>(src + h);
+    if (threadIdx.x == 0) {
+      ys[r] = y[p];
+      if (scale) ss[r] = scale[p];
+    }
   }
 }
 
@@ -99,11 +192,12 @@ template <typename T>
 struct LogitsArgs {
   Operand<T> W;  // A: [V, H], K = H contiguous
   Operand<T> X;  // B: chunk tokens [rows, H]
-  int64_t V, H, rows, nvt, nct, ldz;
+  int64_t V, H, nvt, ldz;
+  RowCount rc;     // the chunk's rows
   int64_t nvh;     // 128-wide vocabulary half tiles: 2 nvt
   T* z;            // chunk buffer [rows, ldz]
   float2* part;    // [rows, nvh] (max, sum of exp) per half tile
-  TileQueue queue; // over nvt x nct tiles
+  TileQueue queue; // over nvt x ceil(rows / 256) tiles (total set in the kernel)
 };
 
 __device__ __forceinline__ void store4(Rsrc r, uint32_t off, float a, float b, float c, float d, __bf16*) {
@@ -143,14 +237,20 @@ constexpr int kNonTemporal = 2;
 template <typename T>
 __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char smem[kGemmLdsBytes];
-  const int tile = take_tile(a.queue, smem);
+  const int64_t rows = a.rc.get();
+  const int64_t nct = (rows + kTile - 1) / kTile;
+  TileQueue q = a.queue;
+  q.total = (int)(a.nvt * nct);
+  const int tile = take_tile(q, smem);
   if (tile < 0) return;
   int64_t vt, ct;
-  grouped_tile(tile, a.nvt, a.nct, kTileGroup, vt, ct);
+  grouped_tile(tile, a.nvt, nct, kTileGroup, vt, ct);
   const int64_t v0 = vt * kTile, c0 = ct * kTile;
+  Operand<T> X = a.X;
+  X.rows = rows;  // rows past the chunk's read as zero
 
   f32x16 acc[4][4];
-  gemm_mainloop<T, false, false>(smem, a.W, v0, a.X, c0, 0, a.H, acc);
+  gemm_mainloop<T, false, false>(smem, a.W, v0, X, c0, 0, a.H, acc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wy = wave >> 1, wx = wave & 1;
@@ -162,7 +262,7 @@ __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
   const int64_t cw = c0 + wx * 128 + (lane & 31);
   const bool full = v0 + wy * 128 + 128 <= a.V;
   const int64_t half = 2 * vt + wy;
-  const int64_t nrows = a.rows - c0 < kTile ? a.rows - c0 : kTile;
+  const int64_t nrows = rows - c0 < kTile ? rows - c0 : kTile;
   const bool store_z = a.z != nullptr;  // forward only: statistics, no chunk buffer
   const Rsrc zr = make_rsrc(store_z ? a.z + c0 * a.ldz : a.W.base, store_z ? nrows * a.ldz * (int64_t)sizeof(T) : 0);
   const uint32_t lane_off = (uint32_t)(((wx * 128 + (lane & 31)) * a.ldz + vw) * (int64_t)sizeof(T));
@@ -203,7 +303,7 @@ __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
     sum += __shfl_xor(sum, 32);
     if (m == kPad) sum = 0.f;  // no entry of this block lies below V
     const int64_t c = cw + 32 * j;
-    if (lane < 32 && c < a.rows) a.part[c * a.nvh + half] = float2{m, sum};
+    if (lane < 32 && c < rows) a.part[c * a.nvh + half] = float2{m, sum};
     // z - m, rounded to the chunk's element type: the entries that carry
     // most of the softmax mass are then small numbers and keep their
     // precision.  Rows are padded to a multiple of 256, so a tile never
@@ -254,15 +354,18 @@ __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
 // One wave per token: combine the half-tile statistics into lse, and take the
 // target's logit as the dot product x_c . w_y in fp32 (the same products the
 // MFMA accumulates, summed in a different order).
+// The token loss of chunk row c goes to rowloss[rowidx[c]] (token
+// compaction) or rowloss[c].
 template <typename T>
 __global__ __launch_bounds__(256) void k_lse(const float2* __restrict__ part, int64_t nvh, const T* __restrict__ X,
                                              const T* __restrict__ W, int64_t H, int64_t V,
-                                             const int64_t* __restrict__ y, int64_t ign, int64_t rows,
-                                             float* __restrict__ lse, float* __restrict__ rowloss) {
+                                             const int64_t* __restrict__ y, int64_t ign, RowCount rc,
+                                             const int32_t* __restrict__ rowidx, float* __restrict__ lse,
+                                             float* __restrict__ rowloss) {
   constexpr int E = Elem<T>::chunk;
   const int lane = threadIdx.x & 63;
   const int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (c >= rows) return;
+  if (c >= rc.get()) return;
   const float2* p = part + c * nvh;
   float M = -FLT_MAX;
   for (int64_t t = lane; t < nvh; t += 64) M = fmaxf(M, p[t].x);
@@ -300,7 +403,7 @@ __global__ __launch_bounds__(256) void k_lse(const float2* __restrict__ part, in
   if (lane == 0) {
     const float l = M + logf(S);
     lse[c] = l;
-    rowloss[c] = (t != ign) ? l - zt : 0.f;
+    rowloss[rowidx ? (int64_t)rowidx[c] : c] = (t != ign) ? l - zt : 0.f;
   }
 }
 
@@ -316,9 +419,11 @@ template <typename T>
 __global__ __launch_bounds__(kGradThreads) void k_grad(T* __restrict__ z, int64_t ldz, int64_t V,
                                               const float* __restrict__ lse, const float2* __restrict__ part,
                                               int64_t nvh, const int64_t* __restrict__ y, int64_t ign,
-                                              const int32_t* __restrict__ nvalid, const float* __restrict__ scale) {
+                                              const int32_t* __restrict__ nvalid, const float* __restrict__ scale,
+                                              RowCount rc) {
   constexpr int E = Elem<T>::chunk;
   const int64_t c = blockIdx.x;
+  if (c >= rc.get()) return;
   const int64_t t = y[c];
   T* row = z + c * ldz;
   if (t == ign) {
@@ -384,9 +489,11 @@ template <typename T>
 struct DxArgs {
   Operand<T> G;  // chunk buffer [rows, ldz], K = V contiguous: the GEMM's B (columns c)
   Operand<T> W;  // [V, H] read K-major: the GEMM's A (rows h)
-  int64_t V, H, rows, nmt, nnt, ksplit, splits;
-  T* dx;         // [rows, H] when not split
-  float* part;   // [splits, rows, H] when split
+  int64_t V, H, nmt, nnt, ksplit, splits;
+  RowCount rc;   // the chunk's rows (nmt: tiles over rc.max)
+  T* dx;         // when not split: chunk row c goes to dx row rowidx[c] (or c)
+  const int32_t* rowidx;
+  float* part;   // [splits, rc.max, H] when split
 };
 
 template <typename T>
@@ -401,9 +508,12 @@ __global__ __launch_bounds__(256) void k_dx(DxArgs<T> a) {
   int64_t mt, nt;
   grouped_tile(t - split * ntiles, a.nmt, a.nnt, 4, mt, nt);
   const int64_t m0 = mt * kTile, n0 = nt * kTile;
+  const int64_t rows = a.rc.get();
+  if (m0 >= rows) return;
   const int64_t k0 = split * a.ksplit;
   const int64_t k1 = k0 + a.ksplit < a.V ? k0 + a.ksplit : a.V;
   Operand<T> G = a.G, W = a.W;
+  G.rows = rows;
   if (k1 < G.cols) G.cols = k1;
   if (k1 < W.rows) W.rows = k1;
 
@@ -416,44 +526,54 @@ __global__ __launch_bounds__(256) void k_dx(DxArgs<T> a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hw = (wave >> 1) * 128 + 4 * (lane >> 5);
   const int cw = (wave & 1) * 128 + (lane & 31);
-  const int mlim = (int)(a.rows - m0 < kTile ? a.rows - m0 : kTile);
+  const int mlim = (int)(rows - m0 < kTile ? rows - m0 : kTile);
   const int nlim = (int)(a.H - n0 < kTile ? a.H - n0 : kTile);
   const bool split_k = a.splits > 1;
-  float* pbase = a.part + split * a.rows * a.H + m0 * a.H + n0;
-  T* dbase = a.dx + m0 * a.H + n0;
+  float* pbase = a.part + split * a.rc.max * a.H + m0 * a.H + n0;
   const uint32_t H = (uint32_t)a.H;
   const bool full = mlim == kTile && nlim == kTile;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int c = cw + 32 * j;
     if (!full && c >= mlim) continue;
+    // this lane's dX row (split partials stay in chunk order)
+    const int64_t drow = a.rowidx ? (int64_t)a.rowidx[m0 + c] : m0 + c;
+    T* drow_base = a.dx + drow * a.H + n0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int h = hw + 32 * i + 8 * g;
         if (full || h < nlim) {
-          const uint32_t off = (uint32_t)c * H + (uint32_t)h;
           const f32x16& q = acc[i][j];
           if (split_k)
-            *reinterpret_cast<f32x4*>(pbase + off) = f32x4{q[4 * g], q[4 * g + 1], q[4 * g + 2], q[4 * g + 3]};
+            *reinterpret_cast<f32x4*>(pbase + ((uint32_t)c * H + (uint32_t)h)) =
+                f32x4{q[4 * g], q[4 * g + 1], q[4 * g + 2], q[4 * g + 3]};
           else
-            store4_ptr(dbase + off, q[4 * g], q[4 * g + 1], q[4 * g + 2], q[4 * g + 3]);
+            store4_ptr(drow_base + h, q[4 * g], q[4 * g + 1], q[4 * g + 2], q[4 * g + 3]);
         }
       }
   }
 }
 
+// dX rows = sum of the split partials [splits][rc.max][H], four consecutive
+// elements per thread (H is a multiple of 4), one row per workgroup pass;
+// chunk row c goes to dx row rowidx[c] (or c).  The partials are read once,
+// with non-temporal loads.
 template <typename T>
-__global__ __launch_bounds__(256) void k_dx_reduce(const float* __restrict__ part, int64_t splits, int64_t n,
+__global__ __launch_bounds__(256) void k_dx_reduce(const float* __restrict__ part, int64_t splits, RowCount rc,
+                                                   int64_t H, const int32_t* __restrict__ rowidx,
                                                    T* __restrict__ dx) {
-  // four consecutive elements per thread (n = rows x H, H a multiple of 4);
-  // the partials are read once, with non-temporal loads
-  const int64_t n4 = n / 4;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t k = 0; k < splits; ++k) s += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(part + k * n) + i);
-    store4_ptr(dx + 4 * i, s[0], s[1], s[2], s[3]);
+  const int64_t rows = rc.get(), pitch = rc.max * H;
+  for (int64_t c = blockIdx.x; c < rows; c += gridDim.x) {
+    const float* src = part + c * H;
+    T* dst = dx + (rowidx ? (int64_t)rowidx[c] : c) * H;
+    for (int64_t h = 4 * (int64_t)threadIdx.x; h < H; h += 4 * 256) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+      for (int64_t k = 0; k < splits; ++k)
+        s += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + k * pitch + h));
+      store4_ptr(dst + h, s[0], s[1], s[2], s[3]);
+    }
   }
 }
 
@@ -464,7 +584,8 @@ struct DwArgs {
   Operand<T> G;   // chunk buffer read K-major ([rows = K][ldz]): the GEMM's B (columns v)
   Operand<T> X;   // fp32: chunk tokens [rows = K][H], read K-major: the GEMM's A (rows h)
   Operand<T> XT;  // bf16: the chunk transposed, [H][ldxt], K-contiguous: the GEMM's A
-  int64_t V, H, rows, nvt, nht;
+  int64_t V, H, nvt, nht;
+  RowCount rc;    // the chunk's rows: the product's K extent
   float* dw;      // [V, H]
   int first;
   TileQueue queue;  // over nvt x nht tiles
@@ -473,9 +594,10 @@ struct DwArgs {
 // X_c^T[h][c] = X_c[c][h] for c < rows, 0 for rows <= c < ldxt (the K tail
 // of the dW product reads whole 16-byte chunks, so the padding must be
 // finite).  64 x 64 tiles through LDS; both global passes are coalesced.
-__global__ __launch_bounds__(256) void k_transpose_chunk(const uint16_t* __restrict__ X, int64_t rows, int64_t H,
+__global__ __launch_bounds__(256) void k_transpose_chunk(const uint16_t* __restrict__ X, RowCount rc, int64_t H,
                                                          uint16_t* __restrict__ XT, int64_t ldxt) {
   __shared__ uint16_t tile[64][66];
+  const int64_t rows = rc.get();
   const int64_t c0 = (int64_t)blockIdx.x * 64, h0 = (int64_t)blockIdx.y * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
 #pragma unroll
@@ -554,6 +676,8 @@ constexpr int kFoldMinStages = FoldOld<kPer>::kStages + 1;
 template <typename T>
 __global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char smem[kGemmLdsBytes];
+  const int64_t rows = a.rc.get();
+  if (rows == 0 && !a.first) return;  // an empty chunk adds nothing
   const int tile = take_tile(a.queue, smem);
   if (tile < 0) return;
   int64_t vt, ht;
@@ -568,13 +692,18 @@ __global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
   // then holds four consecutive h of one dW row
   f32x16 acc[4][4];
   bool folded = false;
+  // K (tokens) past the chunk's rows reads as zero
+  Operand<T> G = a.G;
+  G.rows = rows;
   if constexpr (sizeof(T) == 2) {
-    const int64_t nk = (a.rows + pipe::kBK - 1) / pipe::kBK;
+    Operand<T> XT = a.XT;
+    XT.cols = rows;
+    const int64_t nk = (rows + pipe::kBK - 1) / pipe::kBK;
     auto run = [&](auto& fold) {
       fold.r = pipe::rsrc_words(a.dw + v0 * a.H + h0, ((int64_t)vlim * a.H - h0) * 4);
       fold.voff = (uint32_t)((((wave & 1) * 128 + (lane & 31)) * a.H + (wave >> 1) * 128 + 4 * (lane >> 5)) * 4);
       fold.row32 = (uint32_t)(32 * a.H * 4);
-      gemm_mainloop<T, false, true>(smem, a.XT, h0, a.G, v0, 0, a.rows, acc, fold);
+      gemm_mainloop<T, false, true>(smem, XT, h0, G, v0, 0, rows, acc, fold);
       folded = fold.on;
     };
     if (!a.first && nk >= kFoldMinStages<2> && nk < kFoldMinStages<1>) {
@@ -587,7 +716,9 @@ __global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
       run(fold);
     }
   } else {
-    gemm_mainloop<T, true, true>(smem, a.X, h0, a.G, v0, 0, a.rows, acc);
+    Operand<T> X = a.X;
+    X.rows = rows;
+    gemm_mainloop<T, true, true>(smem, X, h0, G, v0, 0, rows, acc);
   }
 
   // accumulator (i, j, e): h = h0 + (wave / 2) 128 + 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4,
@@ -690,7 +821,28 @@ __global__ __launch_bounds__(1024) void k_loss_final(const float* __restrict__ r
 hipError_t launch_count_valid(const int64_t* y, int64_t BT, int64_t V, int64_t ign, int32_t* nvalid, int32_t* err,
                               hipStream_t s) {
   ProfScope ps(kPhaseCount, s);
-  hipLaunchKernelGGL(k_count_valid, dim3(1), dim3(1024), 0, s, y, BT, V, ign, nvalid, err);
+  hipLaunchKernelGGL(k_count_valid, dim3(1), dim3(1024), 0, s, y, BT, V, ign, nvalid, err, (int32_t*)nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact(const Layout& L, const int64_t* y, int64_t ign, char* ws, int32_t* err, void* dX,
+                          float* rowloss, hipStream_t s) {
+  int32_t* nvalid = reinterpret_cast<int32_t*>(ws + L.off_nvalid);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + L.off_idx);
+  {
+    ProfScope ps(kPhaseCount, s);
+    hipLaunchKernelGGL(k_count_valid, dim3(1), dim3(1024), 0, s, y, L.BT, L.V, ign, nvalid, err, idx);
+  }
+  if (L.BT > 0) {
+    const unsigned blocks = (unsigned)(L.BT < 1024 ? L.BT : 1024);
+    ProfScope ps(kPhaseGather, s);
+    if (L.dtype == 1)
+      hipLaunchKernelGGL(k_zero_ignored<__bf16>, dim3(blocks), dim3(256), 0, s, idx, nvalid, L.BT, L.H,
+                         static_cast<__bf16*>(dX), rowloss);
+    else
+      hipLaunchKernelGGL(k_zero_ignored<float>, dim3(blocks), dim3(256), 0, s, idx, nvalid, L.BT, L.H,
+                         static_cast<float*>(dX), rowloss);
+  }
   return hipGetLastError();
 }
 
@@ -710,71 +862,95 @@ hipError_t launch_loss_final(const float* rowloss, int64_t BT, const int32_t* nv
 }
 
 // Logits of one chunk with their softmax statistics (and, when z is not
-// null, the chunk buffer), then lse and the per-token losses.
+// null, the chunk buffer), then lse and the per-token losses.  Xc, yc: the
+// chunk's rows; row c's token loss goes to rowloss[rowidx[c]] (or [c]).
 template <typename T>
-static void logits_lse(const Layout& L, const T* X, const T* W, const int64_t* y, int64_t ign, int64_t c0,
-                       int64_t rows, char* ws, float* rowloss, T* z, hipStream_t s) {
+static void logits_lse(const Layout& L, const T* Xc, const T* W, const int64_t* yc, int64_t ign, RowCount rc,
+                       const int32_t* rowidx, char* ws, float* rowloss, T* z, hipStream_t s) {
   const int64_t H = L.H, V = L.V;
   float2* part = reinterpret_cast<float2*>(ws + L.off_part);
   float* lse = reinterpret_cast<float*>(ws + L.off_lse);
-  const T* Xc = X + c0 * H;
-  const int64_t* yc = y + c0;
   LogitsArgs<T> la;
   la.W = Operand<T>{W, H, V, H};
-  la.X = Operand<T>{Xc, H, rows, H};
+  la.X = Operand<T>{Xc, H, rc.max, H};
   la.V = V;
   la.H = H;
-  la.rows = rows;
   la.nvt = L.nvt;
+  la.rc = rc;
   la.nvh = 2 * L.nvt;
-  la.nct = (rows + kTile - 1) / kTile;
   la.ldz = L.ldz;
   la.z = z;
   la.part = part;
-  la.queue = TileQueue{reinterpret_cast<int*>(ws + L.off_queue), (int)(la.nvt * la.nct)};
+  // the grid covers rc.max rows; the kernel counts the tiles of the rows in use
+  const int64_t tiles = la.nvt * ((rc.max + kTile - 1) / kTile);
+  la.queue = TileQueue{reinterpret_cast<int*>(ws + L.off_queue), (int)tiles};
   {
     ProfScope ps(kPhaseLogits, s);
     hipLaunchKernelGGL(k_queue_reset, dim3(1), dim3(64), 0, s, la.queue.head);
-    hipLaunchKernelGGL(k_logits<T>, dim3((unsigned)queue_grid(la.queue.total)), dim3(kThreads), 0, s, la);
+    hipLaunchKernelGGL(k_logits<T>, dim3((unsigned)queue_grid(tiles)), dim3(kThreads), 0, s, la);
   }
 
   {
     ProfScope ps(kPhaseLse, s);
-    hipLaunchKernelGGL(k_lse<T>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, part, 2 * L.nvt, Xc, W, H, V, yc,
-                       ign, rows, lse, rowloss + c0);
+    hipLaunchKernelGGL(k_lse<T>, dim3((unsigned)((rc.max + 3) / 4)), dim3(256), 0, s, part, 2 * L.nvt, Xc, W, H, V, yc,
+                       ign, rc, rowidx, lse, rowloss);
   }
 }
 
 template <typename T>
-static hipError_t backward_impl(const Layout& L, const T* X, const T* W, const int64_t* y, const float* scale,
-                                int64_t ign, int64_t c0, int64_t rows, char* ws, T* dX, float* dW, bool first,
-                                hipStream_t s);
+static hipError_t backward_impl(const Layout& L, const T* Xc, const T* W, const int64_t* yc, const float* scalec,
+                                int64_t ign, RowCount rc, const int32_t* rowidx, char* ws, T* dx, float* dW,
+                                bool first, hipStream_t s);
 
+// Chunk c0 .. c0 + rows - 1 of the tokens in their order (no compaction).
 template <typename T>
 static hipError_t chunk_impl(const Layout& L, const T* X, const T* W, const int64_t* y, const float* scale,
                              int64_t ign, int64_t c0, int64_t rows, char* ws, float* rowloss, T* dX, float* dW,
                              bool first, hipStream_t s) {
-  logits_lse<T>(L, X, W, y, ign, c0, rows, ws, rowloss, reinterpret_cast<T*>(ws + L.off_chunk), s);
-  return backward_impl<T>(L, X, W, y, scale, ign, c0, rows, ws, dX, dW, first, s);
+  const RowCount rc{nullptr, 0, rows};
+  logits_lse<T>(L, X + c0 * L.H, W, y + c0, ign, rc, nullptr, ws, rowloss + c0, reinterpret_cast<T*>(ws + L.off_chunk),
+                s);
+  return backward_impl<T>(L, X + c0 * L.H, W, y + c0, scale ? scale + c0 : nullptr, ign, rc, nullptr, ws,
+                          dX + c0 * L.H, dW, first, s);
+}
+
+// Chunk of the non-ignored tokens c0 .. c0 + rows_max - 1 (token
+// compaction): their rows are gathered, the products run on the rows in use,
+// token losses and dX rows go back to the tokens' positions.
+template <typename T>
+static hipError_t chunk_compact_impl(const Layout& L, const T* X, const T* W, const int64_t* y, const float* scale,
+                                     int64_t ign, int64_t c0, int64_t rows_max, char* ws, float* rowloss, T* dX,
+                                     float* dW, bool first, hipStream_t s) {
+  const RowCount rc{reinterpret_cast<const int32_t*>(ws + L.off_nvalid), c0, rows_max};
+  const int32_t* idx = reinterpret_cast<const int32_t*>(ws + L.off_idx);
+  T* xs = reinterpret_cast<T*>(ws + L.off_xs);
+  int64_t* ys = reinterpret_cast<int64_t*>(ws + L.off_ys);
+  float* ss = reinterpret_cast<float*>(ws + L.off_ss);
+  {
+    const unsigned blocks = (unsigned)(rows_max < 4096 ? rows_max : 4096);
+    ProfScope ps(kPhaseGather, s);
+    hipLaunchKernelGGL(k_gather_chunk<T>, dim3(blocks), dim3(256), 0, s, X, y, scale, L.H, idx, rc, xs, ys, ss);
+  }
+  logits_lse<T>(L, xs, W, ys, ign, rc, idx + c0, ws, rowloss, reinterpret_cast<T*>(ws + L.off_chunk), s);
+  return backward_impl<T>(L, xs, W, ys, scale ? ss : nullptr, ign, rc, idx + c0, ws, dX, dW, first, s);
 }
 
 // The backward half of a chunk whose logits (z - M_h) and statistics are in
-// the workspace: in-place gradient, dX rows, dW (+)=.
+// the workspace: in-place gradient, dX rows, dW (+)=.  Xc, yc, scalec: the
+// chunk's rows; chunk row c's dX row goes to dx row rowidx[c] (or c).
 template <typename T>
-static hipError_t backward_impl(const Layout& L, const T* X, const T* W, const int64_t* y, const float* scale,
-                                int64_t ign, int64_t c0, int64_t rows, char* ws, T* dX, float* dW, bool first,
-                                hipStream_t s) {
-  const int64_t H = L.H, V = L.V;
+static hipError_t backward_impl(const Layout& L, const T* Xc, const T* W, const int64_t* yc, const float* scalec,
+                                int64_t ign, RowCount rc, const int32_t* rowidx, char* ws, T* dx, float* dW,
+                                bool first, hipStream_t s) {
+  const int64_t H = L.H, V = L.V, rows = rc.max;
   T* z = reinterpret_cast<T*>(ws + L.off_chunk);
   float2* part = reinterpret_cast<float2*>(ws + L.off_part);
   float* lse = reinterpret_cast<float*>(ws + L.off_lse);
   const int32_t* nvalid = reinterpret_cast<const int32_t*>(ws + L.off_nvalid);
-  const T* Xc = X + c0 * H;
-  const int64_t* yc = y + c0;
   {
     ProfScope ps(kPhaseGrad, s);
-    hipLaunchKernelGGL(k_grad<T>, dim3((unsigned)rows), dim3(kGradThreads), 0, s, z, L.ldz, V, lse, part, 2 * L.nvt, yc, ign,
-                       nvalid, scale ? scale + c0 : nullptr);
+    hipLaunchKernelGGL(k_grad<T>, dim3((unsigned)rows), dim3(kGradThreads), 0, s, z, L.ldz, V, lse, part, 2 * L.nvt, yc,
+                       ign, nvalid, scalec, rc);
   }
 
   // dX = G W
@@ -783,25 +959,24 @@ static hipError_t backward_impl(const Layout& L, const T* X, const T* W, const i
   da.W = Operand<T>{W, H, V, H};
   da.V = V;
   da.H = H;
-  da.rows = rows;
+  da.rc = rc;
   da.nmt = (rows + kTile - 1) / kTile;
   da.nnt = (H + kTile - 1) / kTile;
   const int64_t ks = kStageK<T>;
   da.ksplit = ((V + L.splits - 1) / L.splits + ks - 1) / ks * ks;
   const int64_t splits = (V + da.ksplit - 1) / da.ksplit;
   da.splits = splits;
-  da.dx = dX + c0 * H;
+  da.dx = dx;
+  da.rowidx = rowidx;
   da.part = reinterpret_cast<float*>(ws + L.off_dxpart);
   {
     ProfScope ps(kPhaseDx, s);
     hipLaunchKernelGGL(k_dx<T>, dim3((unsigned)(da.nmt * da.nnt * splits)), dim3(kThreads), 0, s, da);
   }
   if (splits > 1) {
-    const int64_t n = rows * H;
-    int64_t blocks = (n / 4 + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
+    const unsigned blocks = (unsigned)(rows < 8192 ? rows : 8192);
     ProfScope ps(kPhaseDxReduce, s);
-    hipLaunchKernelGGL(k_dx_reduce<T>, dim3((unsigned)blocks), dim3(256), 0, s, da.part, splits, n, da.dx);
+    hipLaunchKernelGGL(k_dx_reduce<T>, dim3(blocks), dim3(256), 0, s, da.part, splits, rc, H, rowidx, dx);
   }
 
   // dW (+)= G^T X_chunk
@@ -812,7 +987,7 @@ static hipError_t backward_impl(const Layout& L, const T* X, const T* W, const i
   wa.XT = Operand<T>{xt, L.ldxt, H, rows};
   wa.V = V;
   wa.H = H;
-  wa.rows = rows;
+  wa.rc = rc;
   wa.nvt = L.nvt;
   wa.nht = (H + kTile - 1) / kTile;
   wa.dw = dW;
@@ -822,7 +997,7 @@ static hipError_t backward_impl(const Layout& L, const T* X, const T* W, const i
     ProfScope ps(kPhaseDw, s);  // bf16: the chunk transpose is counted with the dW product
     if constexpr (sizeof(T) == 2)
       hipLaunchKernelGGL(k_transpose_chunk, dim3((unsigned)(L.ldxt / 64), (unsigned)((H + 63) / 64)), dim3(256), 0, s,
-                         reinterpret_cast<const uint16_t*>(Xc), rows, H, reinterpret_cast<uint16_t*>(xt), L.ldxt);
+                         reinterpret_cast<const uint16_t*>(Xc), rc, H, reinterpret_cast<uint16_t*>(xt), L.ldxt);
     hipLaunchKernelGGL(k_queue_reset, dim3(1), dim3(64), 0, s, wa.queue.head);
     hipLaunchKernelGGL(k_dw<T>, dim3((unsigned)queue_grid(wa.queue.total)), dim3(kThreads), 0, s, wa);
   }
@@ -831,39 +1006,50 @@ static hipError_t backward_impl(const Layout& L, const T* X, const T* W, const i
 
 hipError_t launch_fwd_chunk(const Layout& L, const void* X, const void* W, const int64_t* y, int64_t ign, int64_t c0,
                             int64_t rows, char* ws, float* rowloss, hipStream_t s) {
+  const RowCount rc{nullptr, 0, rows};
   if (L.dtype == 1)
-    logits_lse<__bf16>(L, static_cast<const __bf16*>(X), static_cast<const __bf16*>(W), y, ign, c0, rows, ws, rowloss,
-                       nullptr, s);
+    logits_lse<__bf16>(L, static_cast<const __bf16*>(X) + c0 * L.H, static_cast<const __bf16*>(W), y + c0, ign, rc,
+                       nullptr, ws, rowloss + c0, nullptr, s);
   else
-    logits_lse<float>(L, static_cast<const float*>(X), static_cast<const float*>(W), y, ign, c0, rows, ws, rowloss,
-                      nullptr, s);
+    logits_lse<float>(L, static_cast<const float*>(X) + c0 * L.H, static_cast<const float*>(W), y + c0, ign, rc,
+                      nullptr, ws, rowloss + c0, nullptr, s);
   return hipGetLastError();
 }
 
 hipError_t launch_logits_chunk(const Layout& L, const void* X, const void* W, const int64_t* y, int64_t ign, int64_t c0,
                                int64_t rows, char* ws, float* rowloss, hipStream_t s) {
+  const RowCount rc{nullptr, 0, rows};
   if (L.dtype == 1)
-    logits_lse<__bf16>(L, static_cast<const __bf16*>(X), static_cast<const __bf16*>(W), y, ign, c0, rows, ws, rowloss,
-                       reinterpret_cast<__bf16*>(ws + L.off_chunk), s);
+    logits_lse<__bf16>(L, static_cast<const __bf16*>(X) + c0 * L.H, static_cast<const __bf16*>(W), y + c0, ign, rc,
+                       nullptr, ws, rowloss + c0, reinterpret_cast<__bf16*>(ws + L.off_chunk), s);
   else
-    logits_lse<float>(L, static_cast<const float*>(X), static_cast<const float*>(W), y, ign, c0, rows, ws, rowloss,
-                      reinterpret_cast<float*>(ws + L.off_chunk), s);
+    logits_lse<float>(L, static_cast<const float*>(X) + c0 * L.H, static_cast<const float*>(W), y + c0, ign, rc,
+                      nullptr, ws, rowloss + c0, reinterpret_cast<float*>(ws + L.off_chunk), s);
   return hipGetLastError();
 }
 
 hipError_t launch_grad_chunk(const Layout& L, const void* X, const void* W, const int64_t* y, const float* scale,
                              int64_t ign, int64_t c0, int64_t rows, char* ws, void* dX, float* dW, bool first,
                              hipStream_t s) {
+  const RowCount rc{nullptr, 0, rows};
+  const float* sc = scale ? scale + c0 : nullptr;
   if (L.dtype == 1)
-    return backward_impl<__bf16>(L, static_cast<const __bf16*>(X), static_cast<const __bf16*>(W), y, scale, ign, c0,
-                                 rows, ws, static_cast<__bf16*>(dX), dW, first, s);
-  return backward_impl<float>(L, static_cast<const float*>(X), static_cast<const float*>(W), y, scale, ign, c0, rows,
-                              ws, static_cast<float*>(dX), dW, first, s);
+    return backward_impl<__bf16>(L, static_cast<const __bf16*>(X) + c0 * L.H, static_cast<const __bf16*>(W), y + c0, sc,
+                                 ign, rc, nullptr, ws, static_cast<__bf16*>(dX) + c0 * L.H, dW, first, s);
+  return backward_impl<float>(L, static_cast<const float*>(X) + c0 * L.H, static_cast<const float*>(W), y + c0, sc, ign,
+                              rc, nullptr, ws, static_cast<float*>(dX) + c0 * L.H, dW, first, s);
 }
 
 hipError_t launch_flce_chunk(const Layout& L, const void* X, const void* W, const int64_t* y, const float* scale,
                              int64_t ign, int64_t c0, int64_t rows, char* ws, float* rowloss, void* dX, float* dW,
                              bool first, hipStream_t s) {
+  if (L.compact) {
+    if (L.dtype == 1)
+      return chunk_compact_impl<__bf16>(L, static_cast<const __bf16*>(X), static_cast<const __bf16*>(W), y, scale, ign,
+                                        c0, rows, ws, rowloss, static_cast<__bf16*>(dX), dW, first, s);
+    return chunk_compact_impl<float>(L, static_cast<const float*>(X), static_cast<const float*>(W), y, scale, ign, c0,
+                                     rows, ws, rowloss, static_cast<float*>(dX), dW, first, s);
+  }
   if (L.dtype == 1)
     return chunk_impl<__bf16>(L, static_cast<const __bf16*>(X), static_cast<const __bf16*>(W), y, scale, ign, c0, rows,
                               ws, rowloss, static_cast<__bf16*>(dX), dW, first, s);

@@ -46,7 +46,19 @@ std::string check_layout(const flce::Layout& L, int64_t BT, int64_t H, int64_t V
     if (!a256(o)) return "unaligned offset";
   if (L.off_nvalid + 16 > L.off_queue || L.off_queue % 16 || L.off_queue + 32 > L.off_lse) return "nvalid/queue region";
   if (L.off_lse + (size_t)L.C * 4 > L.off_rowloss) return "lse region";
-  if (L.off_rowloss + (size_t)(BT > 0 ? BT : 1) * 4 > L.off_part) return "rowloss region";
+  if (L.compact) {
+    const size_t coffs[] = {L.off_idx, L.off_ys, L.off_ss, L.off_xs};
+    for (size_t o : coffs)
+      if (!a256(o)) return "unaligned compaction offset";
+    if (L.off_rowloss + (size_t)(BT > 0 ? BT : 1) * 4 > L.off_idx) return "rowloss region";
+    if (L.off_idx + (size_t)(BT > 0 ? BT : 1) * 4 > L.off_ys) return "idx region";
+    if (L.off_ys + (size_t)L.C * 8 > L.off_ss) return "ys region";
+    if (L.off_ss + (size_t)L.C * 4 > L.off_xs) return "ss region";
+    if (L.off_xs + (size_t)L.C * H * es > L.off_part) return "xs region";
+  } else {
+    if (L.off_idx || L.off_ys || L.off_ss || L.off_xs) return "compaction regions without compaction";
+    if (L.off_rowloss + (size_t)(BT > 0 ? BT : 1) * 4 > L.off_part) return "rowloss region";
+  }
   const size_t stats = (size_t)L.C * 2 * L.nvt * 8;
   const size_t xt = L.dtype == FLCE_BF16 ? (size_t)H * L.ldxt * 2 : 0;
   if (L.off_part + stats > L.off_chunk || L.off_part + xt > L.off_chunk) return "statistics region";
@@ -134,7 +146,8 @@ int main() {
       printf("%d\n", flce::check_ce_noalloc(PT<float>(lg), PT<int64_t>(t), BT, V, PT<float>(loss), PT<float>(rl),
                                             PT<int32_t>(err), C));
     } else if (!strcmp(op, "layout") && sscanf(line, "%*s %lld %lld %lld %lld %d", &BT, &H, &V, &C, &dt) == 5) {
-      std::string r = check_layout(flce::make_layout(BT, H, V, C, dt), BT, H, V, C);
+      std::string r = check_layout(flce::make_layout(BT, H, V, C, dt, true), BT, H, V, C);
+      if (r == "ok") r = check_layout(flce::make_layout(BT, H, V, C, dt, false), BT, H, V, C);
       if (r == "ok") r = check_fwd_layout(flce::make_fwd_layout(BT, H, V, C, dt), BT);
       for (int ns = 2; r == "ok" && ns <= 8; ns += 6) {
         if (BT < ns || BT % ns) continue;
@@ -142,22 +155,22 @@ int main() {
         const flce::OrpoLayout O = flce::make_orpo_layout(ns, T, H, V, C, dt);
         if (O.one_pass) {
           const size_t es = dt == 1 ? 2 : 4;
-          if (O.pairs < 1 || O.pairs > B || O.Cp != 2 * O.pairs * T || O.Cp > flce::make_layout(BT, H, V, C, dt).C)
+          if (O.pairs < 1 || O.pairs > B || O.Cp != 2 * O.pairs * T || O.Cp > flce::make_layout(BT, H, V, C, dt, false).C)
             r = "orpo pairs per chunk";
           else if (O.off_nvalid + 12 > O.off_rlc || O.off_rlc + (size_t)O.Cp * 4 > O.off_wc ||
                    O.off_wc + (size_t)O.Cp * 4 > O.off_seq || O.off_seq + (size_t)ns * 24 > O.off_pair ||
                    O.off_pair + (size_t)B * 8 > O.off_xg || O.off_xg + (size_t)O.Cp * H * es > O.off_yg ||
                    O.off_yg + (size_t)O.Cp * 8 > O.off_dxc || O.off_dxc + (size_t)O.Cp * H * es > O.off_region ||
-                   O.off_region + O.fb.total != O.total || !a256(O.off_region) || O.fb.C != O.Cp)
+                   O.off_region + O.fb.total != O.total || !a256(O.off_region) || O.fb.C != O.Cp || O.fb.compact)
             r = "orpo one-pass layout";
         } else {
           const size_t region = O.fwd.total > O.fb.total ? O.fwd.total : O.fb.total;
-          if (O.off_region + region != O.total || !a256(O.off_region) ||
+          if (O.off_region + region != O.total || !a256(O.off_region) || O.fb.compact ||
               O.off_scale + (size_t)BT * 4 > O.off_scratch || O.off_rowloss + (size_t)BT * 4 > O.off_scale)
             r = "orpo layout";
         }
       }
-      if (r == "ok" && flce_workspace_bytes(BT, H, V, C, dt) != (BT < 0 ? 0 : flce::make_layout(BT, H, V, C, dt).total))
+      if (r == "ok" && flce_workspace_bytes(BT, H, V, C, dt) != (BT < 0 ? 0 : flce::make_layout(BT, H, V, C, dt, true).total))
         r = "workspace query";
       printf("%s\n", r.c_str());
     } else if (!strcmp(op, "tiles") && sscanf(line, "%*s %lld", &BT) == 1) {

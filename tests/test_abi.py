@@ -281,13 +281,16 @@ def test_orpo_workspace(lib):
     # chunk's workspace, the gathered rows and their dX rows (4096 x 4096 bf16
     # each), targets, token arrays, per-sequence and per-pair sums
     ws = lib.flce_orpo_workspace_bytes(8, 1024, 4096, 128256, 0, BF16)
-    one = lib.flce_workspace_bytes(4096, 4096, 128256, 4096, BF16)
+    # flce_fwd_bwd's workspace less its token-compaction arrays (positions,
+    # gathered targets, scales and X rows), which the ORPO chunks do not use
+    compaction = 4096 * (4 + 8 + 4) + 4096 * 4096 * 2
+    one = lib.flce_workspace_bytes(4096, 4096, 128256, 4096, BF16) - compaction
     rows = 2 * 4096 * 4096 * 2
     assert one + rows < ws <= one + rows + 4096 * (8 + 4 + 4) + 8 * 24 + 4 * 8 + 8 * 256
     # two passes (a 4096-token sequence pair does not fit a 4096-token chunk):
     # the larger of the two passes' workspaces plus per-token and per-sequence arrays
     ws2 = lib.flce_orpo_workspace_bytes(2, 4096, 4096, 128256, 0, BF16)
-    fb = lib.flce_workspace_bytes(8192, 4096, 128256, 0, BF16)
+    fb = lib.flce_workspace_bytes(8192, 4096, 128256, 0, BF16) - (8192 * 4 + 4096 * (8 + 4) + 4096 * 4096 * 2)
     assert fb < ws2 <= fb + 8192 * 8 + 2 * 24 + 4096
     assert lib.flce_orpo_workspace_bytes(3, 1024, 4096, 128256, 0, BF16) == 0
     assert lib.flce_orpo_workspace_bytes(8, 0, 4096, 128256, 0, BF16) == 0

@@ -31,6 +31,16 @@ def test_roofline_of_an_mfma_kernel():
     assert roof["peak"] == 2500.0
 
 
+def test_roofline_counts_only_the_computed_tokens():
+    # with 410 of 8192 tokens ignored the two dW launches cover 7782 tokens:
+    # 3891 per launch on average
+    w = si.workload("llama3")
+    r = _r({"dw": (3.8, 7.6)}, 4096)
+    r["n_valid"] = 8192 - 410
+    _, roof = bench.roofline(w, r)
+    assert roof["achieved"] == pytest.approx(2.0 * 3891 * 4096 * 128256 / 3.8e-3 / 1e12, rel=1e-4)
+
+
 def test_roofline_of_an_hbm_kernel():
     w = si.workload("llama3")
     name, roof = bench.roofline(w, _r({"grad_inplace": (0.4, 9.0), "dw": (3.8, 7.6)}, 4096))

@@ -153,6 +153,29 @@ def test_out_of_range_target_raises():
     assert e.value.status == 6
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_compaction_leaves_later_chunks_empty(dtype):
+    # only the non-ignored tokens fill the chunks: 70% ignored leaves 360
+    # tokens, chunk 0 full (256), chunk 1 with 104 rows, chunks 2-4 empty
+    check_against_oracle(si.small(1200, 136, 777, dtype, seed=41, ignore=("random_frac", 0.7), w_std=0.05), 256)
+
+
+def test_compaction_tokens_kept_only_at_the_end():
+    # the first 900 positions ignored: the kept tokens all come from the last
+    # chunk's positions, and the ignored dX rows and losses are exact zeros
+    w = si.small(1000, 200, 1000, "bf16", seed=42, w_std=0.05)
+    X, W, y = si.make_inputs(w)
+    y[:900] = w.ignore_index
+    out, _ = check_against_oracle(w, 256, (X, W, y))
+    assert torch.count_nonzero(out["dX"][:900]) == 0 and torch.count_nonzero(out["row_loss"][:900]) == 0
+
+
+def test_compaction_with_split_dx():
+    # 40% ignored and a split dX product: split partials in chunk order, summed
+    # rows written back to the tokens' positions
+    check_against_oracle(si.small(300, 520, 5000, "bf16", seed=43, ignore=("random_frac", 0.4)), 300)
+
+
 def test_custom_ignore_index():
     w = si.small(128, 64, 300, "fp32", seed=29, ignore_index=7, ignore=("random_frac", 0.2))
     check_against_oracle(w, 64)
