@@ -237,8 +237,9 @@ def time_library_gemms(w, Xd, Wd, C, stream, reps=5):
     torch.cuda.empty_cache()
     log("[bench] vendor GEMMs per chunk: " + ", ".join(f"{k} {v['ms']:.3f} ms" for k, v in out.items()))
     out["what"] = (f"torch.mm (hipBLASLt) on one {C}-token chunk: X_c W^T, G W, G^T X_c, bf16 outputs; "
-                   "this library's products also compute the softmax statistics (logits) and accumulate dW in fp32; "
-                   "its chunks hold only the non-ignored tokens (this_library_tokens_per_launch on average)")
+                   "this library's products also compute the softmax statistics (logits) and accumulate dW in fp32, "
+                   "its dX and dW products run as one launch (dx_dw, against the vendor's dx + dw), and its chunks "
+                   "hold only the non-ignored tokens (this_library_tokens_per_launch on average)")
     return out
 
 
@@ -374,10 +375,10 @@ def roofline(w, r):
     # of one call cover N tokens in all: N / nchunks per launch on average.
     n = r.get("n_valid", w.BT)
     per_launch_flops = {
-        # each GEMM launch covers one chunk: 2 * tokens * H * V
+        # each GEMM launch covers one chunk: 2 * tokens * H * V per product
+        # (dX and dW share one launch)
         "logits": 2.0 * n * w.H * w.V / nchunks,
-        "dx": 2.0 * n * w.H * w.V / nchunks,
-        "dw": 2.0 * n * w.H * w.V / nchunks,
+        "dx_dw": 4.0 * n * w.H * w.V / nchunks,
     }
     esz = 2 if w.dtype == "bf16" else 4
     per_launch_bytes = {
@@ -497,7 +498,7 @@ def main(argv=None):
         "orpo": r["orpo"],
         "torch_eager": r["eager"],
         "vendor_gemm_per_chunk": None if r["lib"] is None else dict(
-            r["lib"], this_library_ms={k: round(r["kernels"][k]["avg_ms"], 4) for k in ("logits", "dx", "dw")
+            r["lib"], this_library_ms={k: round(r["kernels"][k]["avg_ms"], 4) for k in ("logits", "dx_dw")
                                        if k in r["kernels"]},
             this_library_tokens_per_launch=round(r["n_valid"] / -(-w.BT // r["C"]), 1)),
         "ce_inplace": ce,

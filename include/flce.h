@@ -210,11 +210,12 @@ int ce_fwd_bwd_inplace_noalloc(float* logits, const int64_t* targets, int64_t BT
  * the recorded events, turns timing off, frees the events and writes, for
  * each kernel kind p < n, the summed duration in ms and the number of timed
  * launches.  Kinds: 0 target count, 1 logits GEMM + softmax statistics,
- * 2 log-sum-exp, 3 in-place logits gradient, 4 dX GEMM, 5 dX split sum,
- * 6 dW GEMM, 7 final mean, 8 logits-only cross-entropy rows, 9 zero fill,
- * 10 ORPO sequence statistics, 11 token compaction (ignored tokens' rows
- * zeroed, each chunk's rows gathered). */
-#define FLCE_NUM_KERNEL_KINDS 12
+ * 2 log-sum-exp, 3 in-place logits gradient, 4 dX and dW GEMMs (one launch,
+ * with the bf16 chunk transpose before it), 5 dX split sum, 6 final mean,
+ * 7 logits-only cross-entropy rows, 8 zero fill, 9 ORPO sequence statistics,
+ * 10 token compaction (ignored tokens' rows zeroed, each chunk's rows
+ * gathered). */
+#define FLCE_NUM_KERNEL_KINDS 11
 int flce_profile_begin(int max_launches);
 int flce_profile_end(double* total_ms, int64_t* launches, int n);
 

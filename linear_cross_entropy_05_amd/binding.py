@@ -372,7 +372,7 @@ def ce_noalloc_max_rows() -> int:
     return int(load_library().ce_noalloc_max_rows())
 
 
-KERNEL_KINDS = ["count_valid", "logits", "lse", "grad_inplace", "dx", "dx_reduce", "dw", "loss_final",
+KERNEL_KINDS = ["count_valid", "logits", "lse", "grad_inplace", "dx_dw", "dx_reduce", "loss_final",
                 "ce_rows", "fill_zero", "orpo_stats", "gather"]
 
 

@@ -15,9 +15,8 @@ enum Phase {
   kPhaseLogits,     // logits GEMM + softmax statistics
   kPhaseLse,        // log-sum-exp combine, per-token loss
   kPhaseGrad,       // in-place gradient of the logits
-  kPhaseDx,         // dX GEMM
+  kPhaseDxDw,       // dX and dW GEMMs (one launch; bf16: with the chunk transpose)
   kPhaseDxReduce,   // sum of dX split partials
-  kPhaseDw,         // dW GEMM
   kPhaseLoss,       // final mean
   kPhaseCeRows,     // logits-only cross-entropy rows
   kPhaseFill,       // zero fill

@@ -755,4 +755,36 @@ __device__ __forceinline__ int take_tile(const TileQueue& q, char* smem) {
   return t;
 }
 
+// Two kinds of work in one launch: n0 items of kind 0 and n1 of kind 1.  The
+// range of XCD x holds its share of kind 0 (xcd_first(n0, x), xcd_len(n0, x)
+// items), taken first, then its share of kind 1; a workgroup takes the next
+// item of its XCD's range, then of another XCD's, as take_tile does.  Returns
+// the item's index within its kind (or -1) and sets `kind`.
+__device__ __forceinline__ int64_t take_item2(int* head, int64_t n0, int64_t n1, char* smem, int& kind) {
+  if (threadIdx.x == 0) {
+    const int x = (int)(blockIdx.x % kXcds);
+    int item = -1, k = 0;
+    for (int i = 0; i < kXcds && item < 0; ++i) {
+      const int y = (x + i) % kXcds;
+      const int v = atomicAdd(head + y, 1);
+      const int l0 = (int)xcd_len(n0, y), l1 = (int)xcd_len(n1, y);
+      if (v < l0) {
+        item = (int)xcd_first(n0, y) + v;
+      } else if (v < l0 + l1) {
+        item = (int)xcd_first(n1, y) + (v - l0);
+        k = 1;
+      }
+    }
+    volatile int* sh = reinterpret_cast<volatile int*>(smem);
+    sh[0] = item;
+    sh[1] = k;
+  }
+  __syncthreads();
+  const volatile int* sh = reinterpret_cast<const volatile int*>(smem);
+  const int item = __builtin_amdgcn_readfirstlane(sh[0]);
+  kind = __builtin_amdgcn_readfirstlane(sh[1]);
+  __syncthreads();
+  return item;
+}
+
 }  // namespace flce

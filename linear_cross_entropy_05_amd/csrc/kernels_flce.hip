@@ -496,20 +496,17 @@ struct DxArgs {
   float* part;   // [splits, rc.max, H] when split
 };
 
+// dX item t of a launch over (split, tile) ids: nmt x nnt tiles cover the
+// chunk's `rows` rows in use, split after split.  The ids are dealt to the
+// XCDs in contiguous ranges, so an XCD's concurrently running tiles are
+// neighbours of one split and share operand blocks in its L2.
 template <typename T>
-__global__ __launch_bounds__(256) void k_dx(DxArgs<T> a) {
-  __shared__ __attribute__((aligned(16))) char smem[kGemmLdsBytes];
-  // one 1-D grid over (split, tile): each XCD walks a contiguous range, so
-  // its concurrently running tiles are neighbours of one split and share
-  // operand blocks in its L2
-  const int64_t ntiles = a.nmt * a.nnt;
-  const int64_t t = xcd_tile(blockIdx.x, ntiles * a.splits);
+__device__ __forceinline__ void dx_item(const DxArgs<T>& a, char* smem, int64_t t, int64_t nmt, int64_t rows) {
+  const int64_t ntiles = nmt * a.nnt;
   const int64_t split = t / ntiles;
   int64_t mt, nt;
-  grouped_tile(t - split * ntiles, a.nmt, a.nnt, 4, mt, nt);
+  grouped_tile(t - split * ntiles, nmt, a.nnt, 4, mt, nt);
   const int64_t m0 = mt * kTile, n0 = nt * kTile;
-  const int64_t rows = a.rc.get();
-  if (m0 >= rows) return;
   const int64_t k0 = split * a.ksplit;
   const int64_t k1 = k0 + a.ksplit < a.V ? k0 + a.ksplit : a.V;
   Operand<T> G = a.G, W = a.W;
@@ -673,13 +670,9 @@ struct FoldOld {
 template <int kPer>
 constexpr int kFoldMinStages = FoldOld<kPer>::kStages + 1;
 
+// dW tile `tile` of nvt x nht over the chunk's `rows` rows in use (its K).
 template <typename T>
-__global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
-  __shared__ __attribute__((aligned(16))) char smem[kGemmLdsBytes];
-  const int64_t rows = a.rc.get();
-  if (rows == 0 && !a.first) return;  // an empty chunk adds nothing
-  const int tile = take_tile(a.queue, smem);
-  if (tile < 0) return;
+__device__ __forceinline__ void dw_item(const DwArgs<T>& a, char* smem, int64_t tile, int64_t rows) {
   int64_t vt, ht;
   // groups of 4 vocabulary tiles (measured ~1% faster than 8 for this product)
   grouped_tile(tile, a.nvt, a.nht, 4, vt, ht);
@@ -795,6 +788,38 @@ __global__ __launch_bounds__(256) void k_dw(DwArgs<T> a) {
       if (j < 3) load_old(2 * j + 3, y);
     }
   }
+}
+
+// ---- dX and dW of a chunk in one launch ------------------------------------------
+
+// Both products read the chunk's gradient and nothing the other writes, so
+// they share one launch and one tile queue: each XCD's range holds its share
+// of the dX items first, then its share of the dW tiles.  The dX items are
+// long (K = V) and go out first, one per CU; a CU whose dX item ends takes dW
+// tiles, so the XCDs' different speeds and the last, partial round of dW
+// tiles spread over the whole launch instead of ending each product.
+template <typename T>
+struct BwdArgs {
+  DxArgs<T> dx;
+  DwArgs<T> dw;
+  int* head;  // kXcds counters, zero at launch
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_dx_dw(BwdArgs<T> a) {
+  __shared__ __attribute__((aligned(16))) char smem[kGemmLdsBytes];
+  const int64_t rows = a.dw.rc.get();
+  const int64_t nmt = (rows + kTile - 1) / kTile;
+  const int64_t ndx = nmt * a.dx.nnt * a.dx.splits;
+  // an empty chunk after the first adds nothing to dW
+  const int64_t ndw = (rows == 0 && !a.dw.first) ? 0 : a.dw.nvt * a.dw.nht;
+  int kind;
+  const int64_t item = take_item2(a.head, ndx, ndw, smem, kind);
+  if (item < 0) return;
+  if (kind == 0)
+    dx_item(a.dx, smem, item, nmt, rows);
+  else
+    dw_item(a.dw, smem, item, rows);
 }
 
 // ---- loss = sum of token losses / N ------------------------------------------------
@@ -969,15 +994,6 @@ static hipError_t backward_impl(const Layout& L, const T* Xc, const T* W, const 
   da.dx = dx;
   da.rowidx = rowidx;
   da.part = reinterpret_cast<float*>(ws + L.off_dxpart);
-  {
-    ProfScope ps(kPhaseDx, s);
-    hipLaunchKernelGGL(k_dx<T>, dim3((unsigned)(da.nmt * da.nnt * splits)), dim3(kThreads), 0, s, da);
-  }
-  if (splits > 1) {
-    const unsigned blocks = (unsigned)(rows < 8192 ? rows : 8192);
-    ProfScope ps(kPhaseDxReduce, s);
-    hipLaunchKernelGGL(k_dx_reduce<T>, dim3(blocks), dim3(256), 0, s, da.part, splits, rc, H, rowidx, dx);
-  }
 
   // dW (+)= G^T X_chunk
   DwArgs<T> wa;
@@ -992,14 +1008,20 @@ static hipError_t backward_impl(const Layout& L, const T* Xc, const T* W, const 
   wa.nht = (H + kTile - 1) / kTile;
   wa.dw = dW;
   wa.first = first ? 1 : 0;
-  wa.queue = TileQueue{reinterpret_cast<int*>(ws + L.off_queue), (int)(wa.nvt * wa.nht)};
+  BwdArgs<T> ba{da, wa, reinterpret_cast<int*>(ws + L.off_queue)};
+  const int64_t items = da.nmt * da.nnt * splits + wa.nvt * wa.nht;
   {
-    ProfScope ps(kPhaseDw, s);  // bf16: the chunk transpose is counted with the dW product
+    ProfScope ps(kPhaseDxDw, s);  // bf16: the chunk transpose is counted with the products
     if constexpr (sizeof(T) == 2)
       hipLaunchKernelGGL(k_transpose_chunk, dim3((unsigned)(L.ldxt / 64), (unsigned)((H + 63) / 64)), dim3(256), 0, s,
                          reinterpret_cast<const uint16_t*>(Xc), rc, H, reinterpret_cast<uint16_t*>(xt), L.ldxt);
-    hipLaunchKernelGGL(k_queue_reset, dim3(1), dim3(64), 0, s, wa.queue.head);
-    hipLaunchKernelGGL(k_dw<T>, dim3((unsigned)queue_grid(wa.queue.total)), dim3(kThreads), 0, s, wa);
+    hipLaunchKernelGGL(k_queue_reset, dim3(1), dim3(64), 0, s, ba.head);
+    hipLaunchKernelGGL(k_dx_dw<T>, dim3((unsigned)queue_grid(items)), dim3(kThreads), 0, s, ba);
+  }
+  if (splits > 1) {
+    const unsigned blocks = (unsigned)(rows < 8192 ? rows : 8192);
+    ProfScope ps(kPhaseDxReduce, s);
+    hipLaunchKernelGGL(k_dx_reduce<T>, dim3(blocks), dim3(256), 0, s, da.part, splits, rc, H, rowidx, dx);
   }
   return hipGetLastError();
 }

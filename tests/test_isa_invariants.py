@@ -24,7 +24,7 @@ sys.path.insert(0, ROOT)
 from linear_cross_entropy_05_amd import build  # noqa: E402
 
 SOURCES = ["kernels_flce.hip", "kernels_ce.hip", "kernels_orpo.hip"]
-DW_BF16 = "_ZN4flce4k_dwIDF16bEEvNS_6DwArgsIT_EE"
+DW_BF16 = "_ZN4flce7k_dx_dwIDF16bEEvNS_7BwdArgsIT_EE"  # the dX and dW products, one kernel
 
 
 @pytest.fixture(scope="module")
@@ -74,7 +74,7 @@ def test_m0_written_only_by_the_copies(asm):
 def test_fold_loads_untouched_until_their_barrier(asm):
     lines = asm["kernels_flce.hip"].splitlines()
     start = next(i for i, l in enumerate(lines) if l.startswith(DW_BF16 + ":"))
-    end = next(i for i in range(start, len(lines)) if "s_endpgm" in lines[i])
+    end = next(i for i in range(start, len(lines)) if lines[i].startswith(".Lfunc_end"))
     raw = lines[start:end]
     code = [l.split(";")[0].strip() for l in raw]
     checked = 0
