@@ -23,11 +23,24 @@ constexpr int64_t xcd_len(int64_t total, int64_t x) { return total / kXcds + (x 
 constexpr int64_t xcd_first(int64_t total, int64_t x) {
   return x * (total / kXcds) + (x < total % kXcds ? x : total % kXcds);
 }
-// Static order over a launch of exactly `total` workgroups: workgroup b takes
-// tile k = b / kXcds of its XCD's range (a bijection onto [0, total)).
-constexpr int64_t xcd_tile(int64_t b, int64_t total) { return xcd_first(total, b % kXcds) + b / kXcds; }
-// Workgroups of a launch whose tiles are taken at run time (TileQueue): one
-// eighth more than the tiles, as many for each XCD.
+// Work items of a launch taken at run time from per-XCD counters (take_item
+// in gemm_core.h): n0 items of kind 0 and n1 of kind 1 (n1 = 0 for a launch
+// of one kind).  The range of XCD y holds its share of kind 0 (items
+// xcd_first(n0, y) .. + xcd_len(n0, y) - 1) and then its share of kind 1;
+// position v of it is the item below, or item -1 past the range.  Over all
+// XCDs and positions each item of each kind appears exactly once.
+struct XcdItem {
+  int64_t item;
+  int kind;
+};
+constexpr XcdItem xcd_item(int64_t n0, int64_t n1, int64_t y, int64_t v) {
+  const int64_t l0 = xcd_len(n0, y), l1 = xcd_len(n1, y);
+  if (v < l0) return XcdItem{xcd_first(n0, y) + v, 0};
+  if (v < l0 + l1) return XcdItem{xcd_first(n1, y) + (v - l0), 1};
+  return XcdItem{-1, 0};
+}
+// Workgroups of such a launch of `total` items: one eighth more than the
+// items, as many for each XCD (the surplus finds every range used up).
 constexpr int64_t queue_grid(int64_t total) {
   return kXcds * ((total + kXcds - 1) / kXcds + ((total + kXcds - 1) / kXcds + 7) / 8);
 }

@@ -720,64 +720,29 @@ __device__ __forceinline__ void grouped_tile(int64_t t, int64_t ntm, int64_t ntn
   tn = l / rows;
 }
 
-// Tiles of one launch handed out at run time.  Each XCD's range of tile ids
-// (xcd_first, xcd_len in flce_host.h) has a counter in `head` (zero at
-// launch).  A workgroup takes the next
-// tile of its XCD's range; once that range is used up, the next tile of
-// another XCD's range.  The XCDs do not run equally fast (a few percent apart
-// on the same tiles), so with tiles fixed per XCD the launch lasts as long as
-// the slowest; here the faster ones take over the rest of its range.  The
-// launch has more workgroups than tiles (queue_grid); a workgroup that finds
-// every range used up returns at once.  Each tile is taken exactly once (one
-// atomic increment per take), and a tile's result does not depend on which
-// workgroup computes it.
-struct TileQueue {
-  int* head;  // kXcds counters
-  int total;
-};
-
-// The tile this workgroup computes, or -1.  Uses the first bytes of `smem`
-// (free before the main loop) to hand thread 0's answer to the workgroup.
-__device__ __forceinline__ int take_tile(const TileQueue& q, char* smem) {
+// Work items of one launch handed out at run time (the layout of the items
+// over the XCDs is xcd_item in flce_host.h).  Each XCD's range has a counter
+// in `head` (kXcds ints, zero at launch).  A workgroup takes the next item of
+// its XCD's range; once that range is used up, the next item of another
+// XCD's range.  The XCDs do not run equally fast (a few percent apart on the
+// same tiles), so with items fixed per XCD the launch lasts as long as the
+// slowest; here the faster ones take over the rest of its range.  The launch
+// has more workgroups than items (queue_grid); a workgroup that finds every
+// range used up gets -1 and returns.  Each item is taken exactly once (one
+// atomic increment per take), and an item's result does not depend on which
+// workgroup computes it.  Uses the first bytes of `smem` (free before the
+// main loop) to hand thread 0's answer to the workgroup; sets `kind`.
+__device__ __forceinline__ int64_t take_item(int* head, int64_t n0, int64_t n1, char* smem, int& kind) {
   if (threadIdx.x == 0) {
     const int x = (int)(blockIdx.x % kXcds);
-    int t = -1;
-    for (int i = 0; i < kXcds && t < 0; ++i) {
+    XcdItem it{-1, 0};
+    for (int i = 0; i < kXcds && it.item < 0; ++i) {
       const int y = (x + i) % kXcds;
-      const int v = atomicAdd(q.head + y, 1);
-      if (v < xcd_len(q.total, y)) t = (int)xcd_first(q.total, y) + v;
-    }
-    *reinterpret_cast<volatile int*>(smem) = t;
-  }
-  __syncthreads();
-  const int t = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(smem));
-  __syncthreads();
-  return t;
-}
-
-// Two kinds of work in one launch: n0 items of kind 0 and n1 of kind 1.  The
-// range of XCD x holds its share of kind 0 (xcd_first(n0, x), xcd_len(n0, x)
-// items), taken first, then its share of kind 1; a workgroup takes the next
-// item of its XCD's range, then of another XCD's, as take_tile does.  Returns
-// the item's index within its kind (or -1) and sets `kind`.
-__device__ __forceinline__ int64_t take_item2(int* head, int64_t n0, int64_t n1, char* smem, int& kind) {
-  if (threadIdx.x == 0) {
-    const int x = (int)(blockIdx.x % kXcds);
-    int item = -1, k = 0;
-    for (int i = 0; i < kXcds && item < 0; ++i) {
-      const int y = (x + i) % kXcds;
-      const int v = atomicAdd(head + y, 1);
-      const int l0 = (int)xcd_len(n0, y), l1 = (int)xcd_len(n1, y);
-      if (v < l0) {
-        item = (int)xcd_first(n0, y) + v;
-      } else if (v < l0 + l1) {
-        item = (int)xcd_first(n1, y) + (v - l0);
-        k = 1;
-      }
+      it = xcd_item(n0, n1, y, atomicAdd(head + y, 1));
     }
     volatile int* sh = reinterpret_cast<volatile int*>(smem);
-    sh[0] = item;
-    sh[1] = k;
+    sh[0] = (int)it.item;
+    sh[1] = it.kind;
   }
   __syncthreads();
   const volatile int* sh = reinterpret_cast<const volatile int*>(smem);

@@ -176,7 +176,8 @@ __global__ __launch_bounds__(256) void k_gather_chunk(const T* __restrict__ X, c
   }
 }
 
-// Counters of a tile queue (TileQueue in gemm_core.h) back to zero before a launch.
+// The per-XCD counters of a launch's work items (take_item in gemm_core.h)
+// back to zero before it.
 __global__ void k_queue_reset(int* head) {
   if (threadIdx.x < kXcds) head[threadIdx.x] = 0;
 }
@@ -197,7 +198,7 @@ struct LogitsArgs {
   int64_t nvh;     // 128-wide vocabulary half tiles: 2 nvt
   T* z;            // chunk buffer [rows, ldz]
   float2* part;    // [rows, nvh] (max, sum of exp) per half tile
-  TileQueue queue; // over nvt x ceil(rows / 256) tiles (total set in the kernel)
+  int* head;       // take_item counters: nvt x ceil(rows / 256) tiles
 };
 
 __device__ __forceinline__ void store4(Rsrc r, uint32_t off, float a, float b, float c, float d, __bf16*) {
@@ -239,9 +240,8 @@ __global__ __launch_bounds__(256) void k_logits(LogitsArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char smem[kGemmLdsBytes];
   const int64_t rows = a.rc.get();
   const int64_t nct = (rows + kTile - 1) / kTile;
-  TileQueue q = a.queue;
-  q.total = (int)(a.nvt * nct);
-  const int tile = take_tile(q, smem);
+  int kind;
+  const int64_t tile = take_item(a.head, a.nvt * nct, 0, smem, kind);
   if (tile < 0) return;
   int64_t vt, ct;
   grouped_tile(tile, a.nvt, nct, kTileGroup, vt, ct);
@@ -585,7 +585,6 @@ struct DwArgs {
   RowCount rc;    // the chunk's rows: the product's K extent
   float* dw;      // [V, H]
   int first;
-  TileQueue queue;  // over nvt x nht tiles
 };
 
 // X_c^T[h][c] = X_c[c][h] for c < rows, 0 for rows <= c < ldxt (the K tail
@@ -814,7 +813,7 @@ __global__ __launch_bounds__(256) void k_dx_dw(BwdArgs<T> a) {
   // an empty chunk after the first adds nothing to dW
   const int64_t ndw = (rows == 0 && !a.dw.first) ? 0 : a.dw.nvt * a.dw.nht;
   int kind;
-  const int64_t item = take_item2(a.head, ndx, ndw, smem, kind);
+  const int64_t item = take_item(a.head, ndx, ndw, smem, kind);
   if (item < 0) return;
   if (kind == 0)
     dx_item(a.dx, smem, item, nmt, rows);
@@ -908,10 +907,10 @@ static void logits_lse(const Layout& L, const T* Xc, const T* W, const int64_t* 
   la.part = part;
   // the grid covers rc.max rows; the kernel counts the tiles of the rows in use
   const int64_t tiles = la.nvt * ((rc.max + kTile - 1) / kTile);
-  la.queue = TileQueue{reinterpret_cast<int*>(ws + L.off_queue), (int)tiles};
+  la.head = reinterpret_cast<int*>(ws + L.off_queue);
   {
     ProfScope ps(kPhaseLogits, s);
-    hipLaunchKernelGGL(k_queue_reset, dim3(1), dim3(64), 0, s, la.queue.head);
+    hipLaunchKernelGGL(k_queue_reset, dim3(1), dim3(64), 0, s, la.head);
     hipLaunchKernelGGL(k_logits<T>, dim3((unsigned)queue_grid(tiles)), dim3(kThreads), 0, s, la);
   }
 

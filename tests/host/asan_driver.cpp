@@ -81,9 +81,9 @@ std::string check_fwd_layout(const flce::Layout& L, int64_t BT) {
   return "ok";
 }
 
-// The per-XCD tile ranges of a launch of `total` tiles partition [0, total)
-// in order, differ in length by at most one, the static order is a bijection,
-// and a queue launch gives every XCD at least as many workgroups as its range.
+// The per-XCD ranges of a launch of `total` items partition [0, total) in
+// order, differ in length by at most one, and a queue launch gives every XCD
+// at least as many workgroups as its range.
 std::string check_tiles(int64_t total) {
   int64_t next = 0, lmin = total, lmax = 0;
   for (int x = 0; x < flce::kXcds; ++x) {
@@ -97,14 +97,30 @@ std::string check_tiles(int64_t total) {
   if (next != total) return "ranges do not cover the launch";
   if (lmax - lmin > 1) return "ranges unbalanced";
   if (flce::queue_grid(total) % flce::kXcds) return "queue grid not a multiple of the XCDs";
-  if (total <= 4096) {
-    std::string seen((size_t)total, '0');
-    for (int64_t b = 0; b < total; ++b) {
-      const int64_t t = flce::xcd_tile(b, total);
-      if (t < 0 || t >= total || seen[(size_t)t] != '0') return "static order not a bijection";
-      seen[(size_t)t] = '1';
+  return "ok";
+}
+
+// Two kinds of items in one launch (n0 then n1 per XCD range): every item of
+// each kind is at exactly one (XCD, position), kind 0 before kind 1 within a
+// range, nothing past the range, and the queue grid covers each range.
+std::string check_items(int64_t n0, int64_t n1) {
+  std::string seen0((size_t)n0, '0'), seen1((size_t)n1, '0');
+  for (int y = 0; y < flce::kXcds; ++y) {
+    const int64_t len = flce::xcd_len(n0, y) + flce::xcd_len(n1, y);
+    if (flce::queue_grid(n0 + n1) / flce::kXcds < len) return "queue grid short for two kinds";
+    int last_kind = 0;
+    for (int64_t v = 0; v < len; ++v) {
+      const flce::XcdItem it = flce::xcd_item(n0, n1, y, v);
+      if (it.kind < last_kind) return "kind 1 before kind 0";
+      last_kind = it.kind;
+      std::string& seen = it.kind ? seen1 : seen0;
+      const int64_t n = it.kind ? n1 : n0;
+      if (it.item < 0 || it.item >= n || seen[(size_t)it.item] != '0') return "item map not a bijection";
+      seen[(size_t)it.item] = '1';
     }
+    if (flce::xcd_item(n0, n1, y, len).item != -1) return "item past the range";
   }
+  if (seen0.find('0') != std::string::npos || seen1.find('0') != std::string::npos) return "item never taken";
   return "ok";
 }
 
@@ -178,6 +194,12 @@ int main() {
       for (int64_t n = 0; n <= BT && r == "ok"; ++n) r = check_tiles(n);
       for (int64_t n : {(int64_t)8016, (int64_t)16032, (int64_t)(1 << 30) - 1, (int64_t)(1 << 30)})
         if (r == "ok") r = check_tiles(n);
+      // dX items then dW tiles: small sizes exhaustively, then the heads' shapes
+      for (int64_t a = 0; a <= 40 && r == "ok"; ++a)
+        for (int64_t b = 0; b <= 40 && r == "ok"; ++b) r = check_items(a, b);
+      for (int64_t a : {(int64_t)240, (int64_t)256, (int64_t)1274, (int64_t)768})
+        for (int64_t b : {(int64_t)8016, (int64_t)8316, (int64_t)12000, (int64_t)1000})
+          if (r == "ok") r = check_items(a, b);
       printf("%s\n", r.c_str());
     } else if (!strcmp(op, "query") && sscanf(line, "%*s %lld %lld %lld %lld %d", &BT, &H, &V, &C, &dt) == 5) {
       printf("%lld,%zu,%zu,%zu,%zu\n", (long long)flce_chunk_tokens(BT, H, V, C, dt),

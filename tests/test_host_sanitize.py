@@ -98,7 +98,8 @@ def test_size_queries_reject_huge_sizes_under_sanitizers(driver):
     assert all(int(v) > 0 for v in got[5].split(",")[:3]), got[5]
 
 
-def test_xcd_tile_ranges_under_sanitizers(driver):
+def test_xcd_ranges_under_sanitizers(driver):
     # every launch size up to 20,000 tiles plus the Llama head's and the
-    # largest one the checks allow: the per-XCD ranges partition the tiles
+    # largest one the checks allow: the per-XCD ranges partition the tiles;
+    # and the two-kind layout of the dX + dW launch is a bijection per kind
     assert _run(driver, ["tiles 20000"]) == ["ok"]
