@@ -61,8 +61,9 @@ struct Layout {
   // X_c^T shares the statistics region (off_part): the statistics are dead
   // once the gradient pass has run, and X_c^T is only read by the dW product
   size_t off_nvalid, off_lse, off_rowloss, off_part, off_chunk, off_dxpart, total;
-  // eight int32 tile-queue counters of the logits and dW products (zeroed
-  // before each launch), inside the 256 bytes that start at off_nvalid
+  // eight int32 work-item counters (take_item) of the logits launch and of
+  // the dX + dW launch (zeroed before each), inside the 256 bytes that start
+  // at off_nvalid
   size_t off_queue;
   // Token compaction (flce_fwd_bwd): only the non-ignored tokens go through
   // the chunks, packed in their order.  idx [BT] int32 holds their positions,

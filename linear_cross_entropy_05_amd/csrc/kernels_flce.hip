@@ -20,7 +20,11 @@
 //            (0 on ignored tokens), N = number of non-ignored tokens
 //   dX       dX[c,:] = G[c,:] W
 //   dW       dW (+)= G^T X_chunk, fp32, stored on the first chunk
+//            (dX and dW share one launch)
 // and once per call: count N and check targets; loss = sum of token losses / N.
+// In flce_fwd_bwd the chunks hold only the non-ignored tokens (gathered, in
+// their order), so the last chunks may hold fewer rows than launched for:
+// the row count comes from N in device memory (RowCount).
 #include <float.h>
 
 #include "flce_internal.h"
