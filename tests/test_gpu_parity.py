@@ -170,6 +170,12 @@ def test_compaction_tokens_kept_only_at_the_end():
     assert torch.count_nonzero(out["dX"][:900]) == 0 and torch.count_nonzero(out["row_loss"][:900]) == 0
 
 
+def test_compaction_over_several_scan_passes():
+    # 9000 targets: the position list is built in three passes of 4096 (the
+    # last ragged), 30% ignored at random; nine chunks of 1000 kept tokens
+    check_against_oracle(si.small(9000, 64, 300, "fp32", seed=44, ignore=("random_frac", 0.3)), 1000)
+
+
 def test_compaction_with_split_dx():
     # 40% ignored and a split dX product: split partials in chunk order, summed
     # rows written back to the tokens' positions
